@@ -1,0 +1,230 @@
+"""Benchmark of the batched Muon step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one muon_step_batched call over the whole batch: momentum, Frobenius
+normalization, 5 Newton-Schulz iterations and the weight update for every
+matrix, on synthetic seeded inputs already resident in HBM.  The default
+workload is 96 bf16 expert matrices of 2048 x 6144.  Prints one JSON line.
+
+The per-kernel durations come from HIP events that the library records around
+each launch on the same stream during the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "expert matrices orthogonalized/sec + % bf16 MFMA peak (6144×2048, 5 NS steps)"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # dense matrix-core peaks at 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+
+
+def ns_flops(shape, steps, with_square=True):
+    """Algorithmic flops of `steps` iterations: symmetric products count unique entries only."""
+    s, l = min(shape), max(shape)
+    gram = s * (s + 1) * l
+    square = s * s * (s + 1) if with_square else 0
+    prod = 2 * s * s * l
+    return steps * (gram + square + prod), steps * gram, steps * square, steps * prod
+
+
+def elementwise_bytes(shape, esize, call, nesterov):
+    """Algorithmic HBM bytes of the three bandwidth-bound kernels, per matrix."""
+    n = shape[0] * shape[1] * esize
+    if call == "step":
+        # read G, M, write M';  read M' (and G), write X0;  read O, W, write W'
+        return 3 * n, (3 if nesterov else 2) * n, 3 * n
+    # read X;  read X, write X0;  read O, write out
+    return n, 2 * n, 2 * n
+
+
+def make_inputs(wl, device, threads=16):
+    import concurrent.futures
+
+    import torch
+
+    import workloads
+
+    def one(j):
+        raw = workloads.matrix_inputs(wl, j)
+        return j, {k: workloads.cast(v, wl.dtype) for k, v in raw.items()}
+
+    out = [None] * wl.batch
+    with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+        for j, d in ex.map(one, range(wl.batch)):
+            out[j] = {k: v.to(device) for k, v in d.items()}
+    torch.cuda.synchronize(device)
+    return out
+
+
+def cpu_baseline(wl, sample: int):
+    """The float64 oracle on `sample` matrices of the same workload, timed on the host."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = os.cpu_count() or 1
+    host = []
+    for j in range(sample):
+        raw = workloads.matrix_inputs(wl, j)
+        host.append({k: workloads.as_float64(workloads.cast(v, wl.dtype)) for k, v in raw.items()})
+    t0 = time.perf_counter()
+    for h in host:
+        if wl.call == "step":
+            oracle.muon_step(h["w"], h["g"], h["m"], lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov,
+                             steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps)
+        else:
+            oracle.newton_schulz(h["x"], wl.steps, wl.coeffs, wl.eps)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "matrices/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample} of {wl.batch} matrices {list(wl.shapes[0])}, float64 numpy, "
+                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="c2_96x2048x6144")
+    ap.add_argument("--cpu-sample", type=int, default=2, help="matrices timed on the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+              "multi-GPU path (matrices are independent; see the sharding notes in DESIGN.md).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import newton_schulz_03_amd as nsa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    nsa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.standard_workloads()[args.workload]
+    print(f"[bench] generating {wl.name}: {wl.batch} matrices", file=sys.stderr, flush=True)
+    t0 = time.time()
+    ins = make_inputs(wl, dev)
+    print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    shapes = list(wl.shapes)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    ws = nsa.allocate_workspace(shapes, tdt, dev)
+    c = wl.coeffs[2]
+
+    if wl.call == "step":
+        W = [d["w"] for d in ins]
+        G = [d["g"] for d in ins]
+        M = [d["m"] for d in ins]
+
+        def step():
+            nsa.step_batched(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov,
+                             steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps, workspace=ws)
+    else:
+        X = [d["x"] for d in ins]
+        OUT = [torch.empty_like(x) for x in X]
+
+        def step():
+            nsa.ns_batched(X, steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps, out=OUT, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    nsa.timing_reset()
+    nsa.timing_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize(dev)
+    nsa.timing_enable(False)
+    kern = nsa.timing_read()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    esize = 2 if wl.dtype == "bf16" else 4
+    fl = [ns_flops(s, wl.steps, c != 0.0) for s in shapes]
+    alg_total = sum(f[0] for f in fl)
+    alg_prod_launch = sum(2 * min(s) ** 2 * max(s) for s in shapes)
+    alg_gram_launch = sum(min(s) * (min(s) + 1) * max(s) for s in shapes)
+    alg_poly_launch = sum(min(s) ** 2 * (min(s) + 1) for s in shapes)
+    peak = PEAK_TFLOPS[wl.dtype]
+
+    def avg(name):
+        ms, n = kern[name]
+        return ms / n if n else float("nan")
+
+    prod_ms = avg("prod")
+    achieved = alg_prod_launch / (prod_ms * 1e-3) / 1e12
+    per_kernel = {k: {"avg_ms": round(avg(k), 4), "launches": kern[k][1]} for k in nsa.KERNELS}
+    ns_ms = (kern["gram"][0] + kern["poly"][0] + kern["prod"][0]) / args.steps
+    ew = [elementwise_bytes(s, esize, wl.call, wl.nesterov) for s in shapes]
+    for name, idx in (("reduce", 0), ("normalize", 1), ("finish", 2)):
+        b = sum(e[idx] for e in ew)
+        per_kernel[name]["gbs"] = round(b / (avg(name) * 1e-3) / 1e9, 1)
+        per_kernel[name]["hbm_frac"] = round(b / (avg(name) * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
+    for name, flops in (("gram", alg_gram_launch), ("poly", alg_poly_launch), ("prod", alg_prod_launch)):
+        if kern[name][1]:
+            t = flops / (avg(name) * 1e-3) / 1e12
+            per_kernel[name]["tflops"] = round(t, 1)
+            per_kernel[name]["mfma_frac"] = round(t / peak, 3)
+
+    value = wl.batch * args.steps / (total_ms * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "shapes": sorted({tuple(s) for s in shapes}),
+                   "ns_steps": wl.steps, "coeffs": list(wl.coeffs), "call": wl.call,
+                   "nesterov": wl.nesterov, "lr": wl.lr, "beta": wl.beta},
+        "roofline": {"bound": "mfma", "kernel": "prod (X <- aX + BX)", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None},
+        "ns_effective_tflops": round(alg_total / (total_ms / args.steps * 1e-3) / 1e12, 1),
+        "ns_mfma_frac_whole_step": round(alg_total / (total_ms / args.steps * 1e-3) / 1e12 / peak, 4),
+        "ns_kernels_ms_per_step": round(ns_ms, 3),
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the oracle on {args.cpu_sample} matrices", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

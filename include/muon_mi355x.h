@@ -1,0 +1,165 @@
+/*
+ * muon_mi355x.h - C ABI of the batched Muon optimizer step for AMD MI355X (gfx950).
+ *
+ * The operation.  Muon is the optimizer used for almost all weight matrices of
+ * the model described on "How PyTorch Scaled a Near-1T MoE on Europe's Public
+ * Supercomputer" (§Three optimizations that changed the economics, FlexShard
+ * bullet).  Its Newton-Schulz update works on whole matrices; placing whole
+ * experts on one rank lets every rank orthogonalize its own matrices with no
+ * communication, and running Newton-Schulz on the GPU instead of the host CPU
+ * is what shortened the optimizer step there.  Muon keeps one optimizer state
+ * per matrix ("Domyn is training a 1T-parameter MoE on Europe's Jupiter
+ * supercomputer, and published the recipe", §What moved the number).
+ *
+ * For each matrix of a ragged batch, muon_step_batched computes
+ *     M' = beta*M + G                          (momentum, the single state)
+ *     U  = G + beta*M'  if nesterov, else M'
+ *     X0 = U / (||U||_F + eps), transposed when rows > cols (short side)
+ *     k times:  A = X X^T;  B = b*A + c*A*A;  X = a*X + B*X
+ *     O  = X_k, transposed back to rows x cols
+ *     W' = W - lr * sqrt(max(1, rows/cols)) * O
+ * and muon_ns_batched computes O from U = x alone.  The pages fix no
+ * polynomial, step count or epsilon; the usual quintic is
+ * (a, b, c) = (3.4445, -4.7750, 2.0315) with k = 5, and (1.5, -0.5, 0) is the
+ * cubic iteration that converges to the polar factor.
+ *
+ * Conventions shared by every entry point:
+ *  - Matrices are dense, row-major, contiguous: element (i, j) of a rows x cols
+ *    matrix is at ptr[i*cols + j].  One dtype covers every tensor of a call.
+ *  - Device pointers (x, out, w, g, m, workspace) must be 16-byte aligned
+ *    device memory of the current HIP device.  Host arrays (rows, cols, the
+ *    pointer arrays, the parameter structs) are read during the call only.
+ *  - The caller owns every buffer, the workspace included.  The library
+ *    allocates no device memory and keeps no pointer after it returns; it owns
+ *    only a small ring of pinned host staging buffers for the descriptor
+ *    upload, allocated on first use and kept until the process ends.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
+ *    and the call returns without synchronizing.  Buffers must stay alive and
+ *    untouched until the stream has finished the work.  Two calls may run
+ *    concurrently only with distinct workspaces.
+ *  - Every argument is validated before anything is enqueued; on any error
+ *    nothing is launched and the outputs are untouched.  batch == 0 is a no-op
+ *    that returns MUON_OK.
+ *  - NaN and Inf propagate; there is no check.  A zero input gives a zero
+ *    output (eps keeps the normalization finite).
+ *  - Results are deterministic: the kernels use no floating-point atomics.
+ *  - No C++ exception crosses this interface.
+ *
+ * Precision.  MUON_BF16: tensors are bf16; products accumulate in fp32 on the
+ * matrix cores; every stored intermediate (X, A, B, M', W') is rounded to
+ * nearest even.  MUON_FP32: tensors and all arithmetic are fp32.
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of every tensor in a call. */
+typedef enum { MUON_BF16 = 0, MUON_FP32 = 1 } muon_dtype;
+
+/* Return codes. */
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = 1, /* null pointer, dim <= 0, misaligned pointer, bad dtype, steps < 0,
+                               aliasing that is not allowed, non-finite parameter */
+  MUON_ERR_UNSUPPORTED = 2, /* a dimension beyond the supported maximum (MUON_MAX_DIM) */
+  MUON_ERR_WORKSPACE = 3,   /* workspace null or smaller than muon_workspace_bytes() */
+  MUON_ERR_HIP = 4          /* a HIP runtime call or launch failed; see muon_last_error_detail() */
+} muon_status;
+
+/* Largest supported rows or cols of one matrix. */
+#define MUON_MAX_DIM 65536
+
+/* Newton-Schulz settings: X <- a*X + (b*A + c*A^2)*X with A = X X^T, `steps` times,
+ * after X0 = U / (||U||_F + eps).  steps == 0 returns X0.  c == 0 skips A^2. */
+typedef struct {
+  int32_t steps;
+  float a, b, c;
+  float eps;
+} muon_ns_params;
+
+/* Full step settings: learning rate, momentum coefficient, Nesterov flag (0/1). */
+typedef struct {
+  float lr;
+  float beta;
+  int32_t nesterov;
+  muon_ns_params ns;
+} muon_step_params;
+
+/*
+ * Bytes of device workspace a call over this batch needs (the same for
+ * muon_ns_batched and muon_step_batched).  rows[i], cols[i]: shape of matrix i.
+ * Returns SIZE_MAX on invalid arguments (detail in muon_last_error_detail()).
+ * batch == 0 returns 0.  Host-only: launches nothing, needs no GPU.
+ */
+size_t muon_workspace_bytes(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype);
+
+/*
+ * Orthogonalize a ragged batch: out[i] = NS_k(x[i]) (shape rows[i] x cols[i]).
+ *   batch       number of matrices (>= 0)
+ *   rows, cols  host arrays[batch] of shapes, each in [1, MUON_MAX_DIM]
+ *   x           host array[batch] of device pointers to the inputs (read only)
+ *   out         host array[batch] of device pointers to the outputs; out[i] may equal x[i]
+ *               (in place) but must not overlap another matrix's buffers otherwise
+ *   dtype       MUON_BF16 or MUON_FP32
+ *   p           Newton-Schulz settings (host pointer)
+ *   workspace   device buffer of at least muon_workspace_bytes() bytes, 256-byte aligned
+ *   stream      hipStream_t to enqueue on
+ */
+int32_t muon_ns_batched(int32_t batch, const int64_t* rows, const int64_t* cols,
+                        const void* const* x, void* const* out, int32_t dtype,
+                        const muon_ns_params* p, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * One Muon step over a ragged batch, in place on w[i] and m[i].
+ *   w           host array[batch] of device pointers to the weights (updated in place)
+ *   g           host array[batch] of device pointers to the gradients (read only)
+ *   m           host array[batch] of device pointers to the momentum buffers (updated in place)
+ *   w[i], g[i], m[i] must be pairwise distinct.  Other arguments as muon_ns_batched.
+ */
+int32_t muon_step_batched(int32_t batch, const int64_t* rows, const int64_t* cols,
+                          void* const* w, const void* const* g, void* const* m, int32_t dtype,
+                          const muon_step_params* p, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Kernels of the step, for per-kernel timing. */
+typedef enum {
+  MUON_K_REDUCE = 0,    /* momentum and per-block sums of squares */
+  MUON_K_NORMALIZE = 1, /* X0 = U / (||U||_F + eps), short side first */
+  MUON_K_GRAM = 2,      /* A = X X^T */
+  MUON_K_POLY = 3,      /* B = b A + c A^2 */
+  MUON_K_PROD = 4,      /* X <- a X + B X */
+  MUON_K_FINISH = 5,    /* W update, or the output copy */
+  MUON_K_COUNT = 6
+} muon_kernel;
+
+/*
+ * Per-kernel timing, off by default.  While enabled (process-wide), every call
+ * records a pair of HIP events on its stream around each kernel launch.
+ * muon_timing_read waits for the recorded events, adds their elapsed times to
+ * per-kernel totals, and returns the total milliseconds and the number of
+ * launches of `kernel` since the last muon_timing_reset.  Returns MUON_OK,
+ * MUON_ERR_INVALID_ARG (bad kernel id or null output) or MUON_ERR_HIP.
+ */
+int32_t muon_timing_enable(int32_t enable);
+int32_t muon_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+int32_t muon_timing_reset(void);
+
+/* Static string naming a status code. */
+const char* muon_status_string(int32_t status);
+
+/* Detail of the last error returned on this thread ("" if none).  Valid until the
+ * next call on this thread. */
+const char* muon_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,12 @@
+"""Batched Muon optimizer step for AMD MI355X (gfx950).
+
+The computation lives in the HIP library libmuon_mi355x.so (C ABI declared in
+include/muon_mi355x.h); this package is its Python binding.
+"""
+from ._binding import (  # noqa: F401
+    CUBIC, EXPORTED, HEADER_PATH, LIB_PATH, MAX_DIM, MUON_BF16, MUON_ERR_HIP,
+    MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_FP32, MUON_OK, QUINTIC,
+    MuonError, NsParams, StepParams, allocate_workspace, last_error_detail, load_library,
+    ns_batched, status_string, step_batched, workspace_bytes, KERNELS, timing_enable,
+    timing_read, timing_reset,
+)

@@ -1,0 +1,249 @@
+"""ctypes binding of libmuon_mi355x.so: argument marshalling only.
+
+Every step of the computation runs in the HIP library.  torch is used for
+device memory (tensors, the workspace) and for the current HIP stream.  If the
+library is missing the calls raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmuon_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "muon_mi355x.h")
+
+MUON_BF16, MUON_FP32 = 0, 1
+MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_ERR_HIP = range(5)
+MAX_DIM = 65536
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+CUBIC = (1.5, -0.5, 0.0)
+
+EXPORTED = ("muon_workspace_bytes", "muon_ns_batched", "muon_step_batched",
+            "muon_status_string", "muon_last_error_detail", "muon_timing_enable",
+            "muon_timing_read", "muon_timing_reset")
+KERNELS = ("reduce", "normalize", "gram", "poly", "prod", "finish")
+
+
+class MuonError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}: {detail}")
+
+
+class NsParams(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                ("c", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+class StepParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta", ctypes.c_float), ("nesterov", ctypes.c_int32),
+                ("ns", NsParams)]
+
+
+_lib_handle: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m newton_schulz_03_amd.build, or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    i32, i64p, vpp, vp, sz = (ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                              ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_size_t)
+    lib.muon_workspace_bytes.argtypes = [i32, i64p, i64p, i32]
+    lib.muon_workspace_bytes.restype = sz
+    lib.muon_ns_batched.argtypes = [i32, i64p, i64p, vpp, vpp, i32, ctypes.POINTER(NsParams), vp,
+                                    sz, vp]
+    lib.muon_ns_batched.restype = i32
+    lib.muon_step_batched.argtypes = [i32, i64p, i64p, vpp, vpp, vpp, i32,
+                                      ctypes.POINTER(StepParams), vp, sz, vp]
+    lib.muon_step_batched.restype = i32
+    lib.muon_status_string.argtypes = [i32]
+    lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_last_error_detail.argtypes = []
+    lib.muon_last_error_detail.restype = ctypes.c_char_p
+    lib.muon_timing_enable.argtypes = [i32]
+    lib.muon_timing_enable.restype = i32
+    lib.muon_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.muon_timing_read.restype = i32
+    lib.muon_timing_reset.argtypes = []
+    lib.muon_timing_reset.restype = i32
+    _lib_handle = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().muon_status_string(status).decode()
+
+
+def last_error_detail() -> str:
+    return load_library().muon_last_error_detail().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != MUON_OK:
+        raise MuonError(status, where, last_error_detail())
+
+
+def _i64_array(vals: Sequence[int]):
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+
+
+def _ptr_array(vals: Sequence[int]):
+    return (ctypes.c_void_p * max(1, len(vals)))(*vals)
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+
+    if dtype == torch.bfloat16:
+        return MUON_BF16
+    if dtype == torch.float32:
+        return MUON_FP32
+    raise TypeError(f"unsupported dtype {dtype}: use torch.bfloat16 or torch.float32")
+
+
+def workspace_bytes(shapes: Sequence[Tuple[int, int]], dtype) -> int:
+    """Device workspace bytes for a batch of (rows, cols) shapes."""
+    lib = load_library()
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    rows = _i64_array([int(r) for r, _ in shapes])
+    cols = _i64_array([int(c) for _, c in shapes])
+    n = lib.muon_workspace_bytes(len(shapes), rows, cols, code)
+    if n == SIZE_MAX:
+        raise MuonError(MUON_ERR_INVALID_ARG, "muon_workspace_bytes", last_error_detail())
+    return int(n)
+
+
+def allocate_workspace(shapes, dtype, device):
+    """A uint8 device tensor usable as the workspace of a call over `shapes`."""
+    import torch
+
+    n = workspace_bytes(shapes, dtype)
+    ws = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + max(n, 1)]
+
+
+def _stream_handle(device) -> int:
+    import torch
+
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensors(ts, name):
+    import torch
+
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError(f"{name}: tensors must live on a HIP device, got {dev}")
+    for t in ts:
+        if t.device != dev or t.dtype != ts[0].dtype:
+            raise ValueError(f"{name}: every tensor must share one device and dtype")
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name}: tensors must be contiguous 2-D matrices")
+    return dev
+
+
+def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
+               out: Optional[Sequence] = None, workspace=None) -> List:
+    """Newton-Schulz orthogonalization of a ragged batch of matrices on the GPU.
+
+    Returns the outputs (new tensors, or `out` when given; out[i] may be xs[i]).
+    Runs on the current HIP stream of the tensors' device.
+    """
+    import torch
+
+    lib = load_library()
+    xs = list(xs)
+    if not xs:
+        return []
+    dev = _check_tensors(xs, "xs")
+    if out is None:
+        out = [torch.empty_like(x) for x in xs]
+    out = list(out)
+    if len(out) != len(xs):
+        raise ValueError("out must have one tensor per input")
+    _check_tensors(out + xs, "out")
+    shapes = [tuple(x.shape) for x in xs]
+    if any(tuple(o.shape) != s for o, s in zip(out, shapes)):
+        raise ValueError("out shapes must match the inputs")
+    code = _dtype_code(xs[0].dtype)
+    if workspace is None:
+        workspace = allocate_workspace(shapes, xs[0].dtype, dev)
+    a, b, c = (float(v) for v in coeffs)
+    p = NsParams(int(steps), a, b, c, float(eps))
+    with torch.cuda.device(dev):
+        st = lib.muon_ns_batched(len(xs), _i64_array([s[0] for s in shapes]),
+                                 _i64_array([s[1] for s in shapes]),
+                                 _ptr_array([x.data_ptr() for x in xs]),
+                                 _ptr_array([o.data_ptr() for o in out]), code, ctypes.byref(p),
+                                 ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                 ctypes.c_void_p(_stream_handle(dev)))
+    _check(st, "muon_ns_batched")
+    return out
+
+
+def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, beta: float = 0.95,
+                 nesterov: bool = False, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
+                 workspace=None) -> None:
+    """One Muon step over a ragged batch, in place on ws (weights) and ms (momentum)."""
+    import torch
+
+    lib = load_library()
+    ws, gs, ms = list(ws), list(gs), list(ms)
+    if not (len(ws) == len(gs) == len(ms)):
+        raise ValueError("ws, gs and ms must have the same length")
+    if not ws:
+        return
+    dev = _check_tensors(ws + gs + ms, "ws/gs/ms")
+    shapes = [tuple(w.shape) for w in ws]
+    if any(tuple(g.shape) != s or tuple(m.shape) != s for g, m, s in zip(gs, ms, shapes)):
+        raise ValueError("w, g and m of one matrix must share a shape")
+    code = _dtype_code(ws[0].dtype)
+    if workspace is None:
+        workspace = allocate_workspace(shapes, ws[0].dtype, dev)
+    a, b, c = (float(v) for v in coeffs)
+    p = StepParams(float(lr), float(beta), 1 if nesterov else 0, NsParams(int(steps), a, b, c,
+                                                                         float(eps)))
+    with torch.cuda.device(dev):
+        st = lib.muon_step_batched(len(ws), _i64_array([s[0] for s in shapes]),
+                                   _i64_array([s[1] for s in shapes]),
+                                   _ptr_array([w.data_ptr() for w in ws]),
+                                   _ptr_array([g.data_ptr() for g in gs]),
+                                   _ptr_array([m.data_ptr() for m in ms]), code, ctypes.byref(p),
+                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                   ctypes.c_void_p(_stream_handle(dev)))
+    _check(st, "muon_step_batched")
+
+
+def timing_enable(on: bool = True) -> None:
+    """Record HIP events around every kernel launch (process-wide) while on."""
+    _check(load_library().muon_timing_enable(1 if on else 0), "muon_timing_enable")
+
+
+def timing_reset() -> None:
+    _check(load_library().muon_timing_reset(), "muon_timing_reset")
+
+
+def timing_read() -> dict:
+    """{kernel name: (total milliseconds, launches)} since the last reset."""
+    lib = load_library()
+    out = {}
+    for k, name in enumerate(KERNELS):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(lib.muon_timing_read(k, ctypes.byref(ms), ctypes.byref(n)), "muon_timing_read")
+        out[name] = (ms.value, n.value)
+    return out

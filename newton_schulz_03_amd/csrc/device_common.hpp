@@ -1,0 +1,125 @@
+// Device helpers shared by the kernels: element types, bf16 rounding,
+// deterministic reductions, batch/tile lookup and the XCD-aware block order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon_internal.hpp"
+
+namespace muon {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Storage types: bf16 is carried as its raw 16 bits.
+struct bf16_tag {};
+
+template <typename T> struct Elt;
+
+template <> struct Elt<uint16_t> {
+  static constexpr int kVec = 8;  // elements per 16-byte vector
+  static __device__ __forceinline__ float to_f32(uint16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  }
+  // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+  static __device__ __forceinline__ uint16_t from_f32(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+  }
+};
+
+template <> struct Elt<float> {
+  static constexpr int kVec = 4;
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float f) { return f; }
+};
+
+// Unpack / pack one 16-byte vector of T into / from fp32 values.
+template <typename T>
+__device__ __forceinline__ void vec_to_f32(const u32x4_t& v, float* out) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(v[i] << 16);
+      out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4_t f32_to_vec(const float* in) {
+  u32x4_t v;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = Elt<uint16_t>::from_f32(in[2 * i]);
+      uint32_t hi = Elt<uint16_t>::from_f32(in[2 * i + 1]);
+      v[i] = lo | (hi << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(in[i]);
+  }
+  return v;
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const u32x4_t& v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+// Sum over a wavefront of 64 lanes with a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum over a block of kThreads threads; every thread gets the result.
+template <typename F>
+__device__ __forceinline__ F block_sum(F v, F* scratch /* kThreads/64 entries */) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  F t = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+// Index j with prefix[j] <= b < prefix[j+1] (prefix is non-decreasing, prefix[0] = 0).
+__device__ __forceinline__ int find_matrix(const int32_t* prefix, int batch, int32_t b) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs of the chip (block b runs on
+// XCD b % 8).  Renumber them so that each XCD receives one contiguous range of
+// logical blocks: neighbouring tiles, which share operands, then share an L2.
+__device__ __forceinline__ int32_t xcd_remap(int32_t b, int32_t n) {
+  constexpr int kXcd = 8;
+  const int32_t xcd = b % kXcd, local = b / kXcd;
+  const int32_t per = n / kXcd, rem = n % kXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+}  // namespace muon

@@ -1,0 +1,273 @@
+// Bandwidth-bound kernels of the Muon step:
+//   k_reduce     momentum M' = beta*M + G (step) and per-block sums of U^2
+//   k_normalize  X0 = U / (||U||_F + eps) in the wide orientation, zero padded
+//   k_finish     W' = W - lr*sqrt(max(1,rows/cols))*O (step) or out = O (orthogonalize only)
+// All three read and write whole 16-byte vectors along rows, so every wavefront
+// touches contiguous runs of memory.  The norm is deterministic: each reduce
+// block writes one partial, and each normalize block sums its matrix's partials
+// in a fixed order.
+#include "device_common.hpp"
+
+namespace muon {
+
+namespace {
+
+template <typename T>
+struct URow {
+  // Loads 16 consecutive elements of U from user row `r`, starting at column c0,
+  // with zeros beyond the row.  U is x (orthogonalize only), M' (step), or
+  // G + beta*M' (Nesterov step).
+  static __device__ __forceinline__ void load(const MatDesc& d, const ElemParams& p, int64_t r,
+                                              int64_t c0, float* u) {
+    constexpr int V = Elt<T>::kVec;
+    const int64_t cols = d.cols;
+    const int64_t rowoff = r * cols;
+#pragma unroll
+    for (int q = 0; q < 16 / V; ++q) {
+      const int64_t col = c0 + q * V;
+      float* o = u + q * V;
+      if (d.vec_ok && col + V <= cols) {
+        const int64_t off = rowoff + col;
+        if (p.mode == MODE_NS) {
+          vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), o);
+        } else {
+          vec_to_f32<T>(ld16(static_cast<const T*>(d.mom) + off), o);
+          if (p.nesterov) {
+            float g[V];
+            vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), g);
+#pragma unroll
+            for (int e = 0; e < V; ++e) o[e] = g[e] + p.beta * o[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          float v = 0.f;
+          if (col + e < cols) {
+            const int64_t off = rowoff + col + e;
+            if (p.mode == MODE_NS) {
+              v = Elt<T>::to_f32(static_cast<const T*>(d.src)[off]);
+            } else {
+              v = Elt<T>::to_f32(static_cast<const T*>(d.mom)[off]);
+              if (p.nesterov) v = Elt<T>::to_f32(static_cast<const T*>(d.src)[off]) + p.beta * v;
+            }
+          }
+          o[e] = v;
+        }
+      }
+    }
+  }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// k_reduce: one block per kThreads*V*kReduceIters elements of one matrix.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_reduce(LaunchCtx c, ElemParams p) {
+  __shared__ float scratch[kThreads / 64];
+  constexpr int V = Elt<T>::kVec;
+  const int32_t* pre = c.prefix + PH_REDUCE * (c.batch + 1);
+  const int32_t b = blockIdx.x;
+  const int j = find_matrix(pre, c.batch, b);
+  const MatDesc& d = c.desc[j];
+  const int64_t numel = d.numel;
+  const int64_t base = static_cast<int64_t>(b - pre[j]) * (int64_t)(kThreads * V * kReduceIters);
+  float acc = 0.f;
+#pragma unroll
+  for (int it = 0; it < kReduceIters; ++it) {
+    const int64_t off = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * V;
+    if (off >= numel) break;
+    const int n = (off + V <= numel) ? V : static_cast<int>(numel - off);
+    float u[V];
+    if (p.mode == MODE_NS) {
+      if (n == V) {
+        vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), u);
+      } else {
+        for (int e = 0; e < V; ++e)
+          u[e] = e < n ? Elt<T>::to_f32(static_cast<const T*>(d.src)[off + e]) : 0.f;
+      }
+    } else {
+      float g[V], m[V];
+      T* mp = static_cast<T*>(d.mom) + off;
+      const T* gp = static_cast<const T*>(d.src) + off;
+      if (n == V) {
+        vec_to_f32<T>(ld16(gp), g);
+        vec_to_f32<T>(ld16(mp), m);
+      } else {
+        for (int e = 0; e < V; ++e) {
+          g[e] = e < n ? Elt<T>::to_f32(gp[e]) : 0.f;
+          m[e] = e < n ? Elt<T>::to_f32(mp[e]) : 0.f;
+        }
+      }
+      float mn[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) mn[e] = p.beta * m[e] + g[e];
+      u32x4_t packed = f32_to_vec<T>(mn);
+      float mr[V];  // the stored (rounded) buffer: U is formed from it, as the next kernel does
+      vec_to_f32<T>(packed, mr);
+      if (n == V) {
+        st16(mp, packed);
+      } else {
+        for (int e = 0; e < n; ++e) mp[e] = Elt<T>::from_f32(mn[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) u[e] = p.nesterov ? g[e] + p.beta * mr[e] : mr[e];
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc += u[e] * u[e];
+  }
+  const float total = block_sum(acc, scratch);
+  if (threadIdx.x == 0) c.partials[b] = total;
+}
+
+// Sum of the matrix's partials in a fixed order, then 1 / (sqrt(sum) + eps).
+__device__ __forceinline__ float inv_norm(const LaunchCtx& c, int j, float eps, double* scratch) {
+  const int32_t* pre = c.prefix + PH_REDUCE * (c.batch + 1);
+  double s = 0.0;
+  for (int32_t k = pre[j] + threadIdx.x; k < pre[j + 1]; k += kThreads) s += c.partials[k];
+  s = block_sum(s, scratch);
+  return static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(eps)));
+}
+
+// ---------------------------------------------------------------------------
+// k_normalize: one block per 64x64 tile of the padded wide iterate X0.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_normalize(LaunchCtx c, ElemParams p) {
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  __shared__ double scratch[kThreads / 64];
+  constexpr int V = Elt<T>::kVec;
+  const int32_t* pre = c.prefix + PH_NORMALIZE * (c.batch + 1);
+  const int32_t b = blockIdx.x;
+  const int j = find_matrix(pre, c.batch, b);
+  const MatDesc& d = c.desc[j];
+  const int32_t t = b - pre[j];
+  const int32_t tpr = d.l_pad / kEwTile;
+  const int64_t i0 = static_cast<int64_t>(t / tpr) * kEwTile;  // wide rows
+  const int64_t j0 = static_cast<int64_t>(t % tpr) * kEwTile;  // wide cols
+  const float inv = inv_norm(c, j, p.eps, scratch);
+  const int rr = threadIdx.x >> 2, cc = (threadIdx.x & 3) * 16;
+  float u[16];
+  if (!d.tall) {
+    if (i0 + rr < d.s) {
+      URow<T>::load(d, p, i0 + rr, j0 + cc, u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) u[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) u[e] *= inv;
+  } else {
+    // wide X0[i][jw] = U[jw][i]: stage the user tile (rows j0.., cols i0..) through LDS
+    if (j0 + rr < d.l) {
+      URow<T>::load(d, p, j0 + rr, i0 + cc, u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) u[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tile[rr][cc + e] = u[e] * inv;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) u[e] = tile[cc + e][rr];
+  }
+  T* x0 = static_cast<T*>(d.x[0]) + (i0 + rr) * d.l_pad + j0 + cc;
+#pragma unroll
+  for (int q = 0; q < 16 / V; ++q) st16(x0 + q * V, f32_to_vec<T>(u + q * V));
+}
+
+// ---------------------------------------------------------------------------
+// k_finish: one block per 64x64 tile of the user-shaped output.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_finish(LaunchCtx c, ElemParams p) {
+  __shared__ float tile[kEwTile][kEwTile + 1];
+  constexpr int V = Elt<T>::kVec;
+  const int32_t* pre = c.prefix + PH_FINISH * (c.batch + 1);
+  const int32_t b = blockIdx.x;
+  const int j = find_matrix(pre, c.batch, b);
+  const MatDesc& d = c.desc[j];
+  const int32_t t = b - pre[j];
+  const int32_t tpr = static_cast<int32_t>((d.cols + kEwTile - 1) / kEwTile);
+  const int64_t r0 = static_cast<int64_t>(t / tpr) * kEwTile;  // user rows
+  const int64_t c0 = static_cast<int64_t>(t % tpr) * kEwTile;  // user cols
+  const int rr = threadIdx.x >> 2, cc = (threadIdx.x & 3) * 16;
+  const T* X = static_cast<const T*>(d.x[p.cur]);
+  float o[16];
+  if (!d.tall) {
+    const T* src = X + (r0 + rr) * d.l_pad + c0 + cc;  // inside the padded buffer
+#pragma unroll
+    for (int q = 0; q < 16 / V; ++q) vec_to_f32<T>(ld16(src + q * V), o + q * V);
+  } else {
+    // O[r][c] = X[c][r]: stage the wide tile (rows c0.., cols r0..) through LDS
+    const T* src = X + (c0 + rr) * d.l_pad + r0 + cc;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16 / V; ++q) vec_to_f32<T>(ld16(src + q * V), v + q * V);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tile[rr][cc + e] = v[e];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = tile[cc + e][rr];
+  }
+  const int64_t r = r0 + rr;
+  if (r >= d.rows) return;
+  const int64_t cols = d.cols;
+  T* dst = static_cast<T*>(d.dst) + r * cols;
+  const float step = p.lr * d.scale;
+#pragma unroll
+  for (int q = 0; q < 16 / V; ++q) {
+    const int64_t col = c0 + cc + q * V;
+    float* oq = o + q * V;
+    if (d.vec_ok && col + V <= cols) {
+      if (p.mode == MODE_STEP) {
+        float w[V];
+        vec_to_f32<T>(ld16(dst + col), w);
+#pragma unroll
+        for (int e = 0; e < V; ++e) oq[e] = w[e] - step * oq[e];
+      }
+      st16(dst + col, f32_to_vec<T>(oq));
+    } else {
+      for (int e = 0; e < V; ++e) {
+        if (col + e >= cols) break;
+        float v = oq[e];
+        if (p.mode == MODE_STEP) v = Elt<T>::to_f32(dst[col + e]) - step * v;
+        dst[col + e] = Elt<T>::from_f32(v);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p) {
+  if (nblocks <= 0) return hipSuccess;
+  if (is_bf16)
+    hipLaunchKernelGGL(k_reduce<uint16_t>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+  else
+    hipLaunchKernelGGL(k_reduce<float>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_normalize(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p) {
+  if (nblocks <= 0) return hipSuccess;
+  if (is_bf16)
+    hipLaunchKernelGGL(k_normalize<uint16_t>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+  else
+    hipLaunchKernelGGL(k_normalize<float>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p) {
+  if (nblocks <= 0) return hipSuccess;
+  if (is_bf16)
+    hipLaunchKernelGGL(k_finish<uint16_t>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+  else
+    hipLaunchKernelGGL(k_finish<float>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,467 @@
+// C ABI of the batched Muon step: argument validation, workspace planning, the
+// descriptor upload and the launch sequence.  See include/muon_mi355x.h for the
+// contract.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "muon_internal.hpp"
+#include "muon_mi355x.h"
+
+namespace muon {
+namespace {
+
+thread_local std::string g_detail;
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return status;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int64_t cdiv(int64_t x, int64_t a) { return (x + a - 1) / a; }
+
+struct Plan {
+  int32_t batch = 0;
+  bool bf16 = true;
+  size_t esize = 2;
+  std::vector<MatDesc> desc;        // workspace pointers filled in by bind()
+  std::vector<size_t> mat_off;      // byte offset of matrix i's buffers
+  std::vector<int32_t> prefix;      // NPHASE x (batch + 1)
+  int32_t totals[NPHASE] = {0, 0, 0, 0, 0};
+  size_t table_bytes = 0;
+  size_t partials_off = 0;
+  size_t total_bytes = 0;
+};
+
+// Shapes and counts only; no pointers.  Returns MUON_OK or an error (with detail).
+int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype, Plan& pl) {
+  if (batch < 0) return fail(MUON_ERR_INVALID_ARG, "batch = %d is negative", batch);
+  if (dtype != MUON_BF16 && dtype != MUON_FP32)
+    return fail(MUON_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (batch > 0 && (rows == nullptr || cols == nullptr))
+    return fail(MUON_ERR_INVALID_ARG, "rows/cols array is null");
+  pl.batch = batch;
+  pl.bf16 = dtype == MUON_BF16;
+  pl.esize = pl.bf16 ? 2 : 4;
+  const int64_t vec = 16 / static_cast<int64_t>(pl.esize);
+  const int64_t reduce_elems = static_cast<int64_t>(kThreads) * vec * kReduceIters;
+  pl.desc.assign(batch, MatDesc{});
+  pl.mat_off.assign(batch, 0);
+  pl.prefix.assign(static_cast<size_t>(NPHASE) * (batch + 1), 0);
+  int64_t tot[NPHASE] = {0, 0, 0, 0, 0};
+  for (int32_t i = 0; i < batch; ++i) {
+    const int64_t r = rows[i], c = cols[i];
+    if (r <= 0 || c <= 0)
+      return fail(MUON_ERR_INVALID_ARG, "matrix %d has shape %lld x %lld", i, (long long)r,
+                  (long long)c);
+    if (r > MUON_MAX_DIM || c > MUON_MAX_DIM)
+      return fail(MUON_ERR_UNSUPPORTED, "matrix %d has shape %lld x %lld; the maximum side is %d",
+                  i, (long long)r, (long long)c, MUON_MAX_DIM);
+    MatDesc& d = pl.desc[i];
+    d.rows = r;
+    d.cols = c;
+    d.numel = r * c;
+    d.tall = r > c ? 1 : 0;
+    d.s = static_cast<int32_t>(d.tall ? c : r);
+    d.l = static_cast<int32_t>(d.tall ? r : c);
+    d.s_pad = static_cast<int32_t>(round_up(d.s, kTile));
+    d.l_pad = static_cast<int32_t>(round_up(d.l, kTile));
+    d.vec_ok = (c % vec) == 0 ? 1 : 0;
+    d.scale = static_cast<float>(std::sqrt(std::max(1.0, static_cast<double>(r) / static_cast<double>(c))));
+    const int64_t ts = d.s_pad / kTile, tl = d.l_pad / kTile;
+    const int64_t cnt[NPHASE] = {
+        cdiv(d.numel, reduce_elems),                                   // PH_REDUCE
+        static_cast<int64_t>(d.s_pad / kEwTile) * (d.l_pad / kEwTile),  // PH_NORMALIZE
+        ts * (ts + 1) / 2,                                             // PH_SYM
+        ts * tl,                                                       // PH_PROD
+        cdiv(r, kEwTile) * cdiv(c, kEwTile),                           // PH_FINISH
+    };
+    for (int ph = 0; ph < NPHASE; ++ph) {
+      pl.prefix[static_cast<size_t>(ph) * (batch + 1) + i] = static_cast<int32_t>(tot[ph]);
+      tot[ph] += cnt[ph];
+      if (tot[ph] > 0x7fffffffLL)
+        return fail(MUON_ERR_UNSUPPORTED, "batch too large: more than 2^31 blocks in one launch");
+    }
+  }
+  for (int ph = 0; ph < NPHASE; ++ph) {
+    pl.prefix[static_cast<size_t>(ph) * (batch + 1) + batch] = static_cast<int32_t>(tot[ph]);
+    pl.totals[ph] = static_cast<int32_t>(tot[ph]);
+  }
+  size_t off = 0;
+  off += align_up(sizeof(MatDesc) * batch, kAlign);
+  off += align_up(sizeof(int32_t) * pl.prefix.size(), kAlign);
+  pl.table_bytes = off;
+  pl.partials_off = off;
+  off += align_up(sizeof(float) * static_cast<size_t>(tot[PH_REDUCE]), kAlign);
+  for (int32_t i = 0; i < batch; ++i) {
+    const MatDesc& d = pl.desc[i];
+    pl.mat_off[i] = off;
+    const size_t xb = align_up(static_cast<size_t>(d.s_pad) * d.l_pad * pl.esize, kAlign);
+    const size_t sb = align_up(static_cast<size_t>(d.s_pad) * d.s_pad * pl.esize, kAlign);
+    off += 2 * xb + 2 * sb;
+  }
+  pl.total_bytes = batch == 0 ? 0 : off;
+  return MUON_OK;
+}
+
+// Fill the workspace pointers of every descriptor.
+void bind(Plan& pl, char* ws) {
+  for (int32_t i = 0; i < pl.batch; ++i) {
+    MatDesc& d = pl.desc[i];
+    const size_t xb = align_up(static_cast<size_t>(d.s_pad) * d.l_pad * pl.esize, kAlign);
+    const size_t sb = align_up(static_cast<size_t>(d.s_pad) * d.s_pad * pl.esize, kAlign);
+    char* base = ws + pl.mat_off[i];
+    d.x[0] = base;
+    d.x[1] = base + xb;
+    d.gram = base + 2 * xb;
+    d.poly = base + 2 * xb + sb;
+  }
+}
+
+// Pinned host staging for the descriptor upload: a ring of slots per device,
+// each guarded by an event recorded after its copy, so that a slot is reused
+// only once the stream has consumed it.
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+constexpr int kRing = 8;
+struct Ring {
+  Slot slot[kRing];
+  int next = 0;
+};
+std::mutex g_ring_mu;
+std::map<int, Ring> g_rings;
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(MUON_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+int32_t upload_table(const Plan& pl, void* ws, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ring_mu);
+  Ring& ring = g_rings[dev];
+  Slot& s = ring.slot[ring.next];
+  ring.next = (ring.next + 1) % kRing;
+  if (s.done == nullptr) {
+    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  if (s.pending) {
+    e = hipEventSynchronize(s.done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging slot)");
+    s.pending = false;
+  }
+  if (s.cap < pl.table_bytes) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(pl.table_bytes, 64 * 1024);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
+    s.cap = cap;
+  }
+  char* h = static_cast<char*>(s.host);
+  std::memset(h, 0, pl.table_bytes);
+  std::memcpy(h, pl.desc.data(), sizeof(MatDesc) * pl.batch);
+  std::memcpy(h + align_up(sizeof(MatDesc) * pl.batch, kAlign), pl.prefix.data(),
+              sizeof(int32_t) * pl.prefix.size());
+  e = hipMemcpyAsync(ws, h, pl.table_bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (descriptor table)");
+  e = hipEventRecord(s.done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  s.pending = true;
+  return MUON_OK;
+}
+
+// Per-kernel timing: pairs of events recorded around each launch while enabled.
+struct TimingRec {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<hipEvent_t> g_event_pool;
+std::vector<TimingRec> g_pending;
+double g_total_ms[MUON_K_COUNT] = {0, 0, 0, 0, 0, 0};
+int64_t g_launches[MUON_K_COUNT] = {0, 0, 0, 0, 0, 0};
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with timing events when timing is enabled.
+struct TimedLaunch {
+  int kernel;
+  hipStream_t stream;
+  hipEvent_t start = nullptr, stop = nullptr;
+  TimedLaunch(int k, hipStream_t s) : kernel(k), stream(s) {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    if (!g_timing_on) return;
+    start = take_event();
+    stop = take_event();
+    if (start && stop) (void)hipEventRecord(start, stream);
+  }
+  void done() {
+    if (!start || !stop) return;
+    (void)hipEventRecord(stop, stream);
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    g_pending.push_back({kernel, start, stop});
+  }
+};
+
+int32_t drain_timing() {
+  for (const TimingRec& r : g_pending) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (timing)");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    g_total_ms[r.kernel] += ms;
+    g_launches[r.kernel] += 1;
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_pending.clear();
+  return MUON_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_ns_params(const muon_ns_params* p) {
+  if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "params pointer is null");
+  if (p->steps < 0) return fail(MUON_ERR_INVALID_ARG, "steps = %d is negative", p->steps);
+  if (!std::isfinite(p->a) || !std::isfinite(p->b) || !std::isfinite(p->c) ||
+      !std::isfinite(p->eps) || p->eps < 0.f)
+    return fail(MUON_ERR_INVALID_ARG, "Newton-Schulz coefficients must be finite and eps >= 0");
+  return MUON_OK;
+}
+
+int32_t check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
+  if (ws == nullptr || ws_bytes < pl.total_bytes)
+    return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed", ws_bytes, ws,
+                pl.total_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+    return fail(MUON_ERR_INVALID_ARG, "workspace pointer %p is not 256-byte aligned", ws);
+  return MUON_OK;
+}
+
+// Enqueue the whole step after the table is in place.
+int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
+            const muon_ns_params& ns) {
+  LaunchCtx c;
+  c.desc = reinterpret_cast<const MatDesc*>(ws);
+  c.prefix = reinterpret_cast<const int32_t*>(ws + align_up(sizeof(MatDesc) * pl.batch, kAlign));
+  c.partials = reinterpret_cast<float*>(ws + pl.partials_off);
+  c.batch = pl.batch;
+  c.stream = stream;
+  hipError_t e;
+  {
+    TimedLaunch t(MUON_K_REDUCE, stream);
+    if ((e = launch_reduce(c, pl.totals[PH_REDUCE], pl.bf16, ep)) != hipSuccess)
+      return hip_fail(e, "launch momentum/sum-of-squares");
+    t.done();
+  }
+  {
+    TimedLaunch t(MUON_K_NORMALIZE, stream);
+    if ((e = launch_normalize(c, pl.totals[PH_NORMALIZE], pl.bf16, ep)) != hipSuccess)
+      return hip_fail(e, "launch normalize");
+    t.done();
+  }
+  const bool use_poly = ns.c != 0.f;
+  int32_t cur = 0;
+  for (int k = 0; k < ns.steps; ++k) {
+    {
+      TimedLaunch t(MUON_K_GRAM, stream);
+      if ((e = launch_gram(c, pl.totals[PH_SYM], pl.bf16, cur)) != hipSuccess)
+        return hip_fail(e, "launch Gram");
+      t.done();
+    }
+    if (use_poly) {
+      TimedLaunch t(MUON_K_POLY, stream);
+      if ((e = launch_poly(c, pl.totals[PH_SYM], pl.bf16, ns.b, ns.c)) != hipSuccess)
+        return hip_fail(e, "launch polynomial");
+      t.done();
+    }
+    {
+      TimedLaunch t(MUON_K_PROD, stream);
+      if ((e = launch_prod(c, pl.totals[PH_PROD], pl.bf16, cur, ns.a, use_poly ? 1.f : ns.b,
+                           use_poly)) != hipSuccess)
+        return hip_fail(e, "launch product");
+      t.done();
+    }
+    cur ^= 1;
+  }
+  ElemParams fp = ep;
+  fp.cur = cur;
+  {
+    TimedLaunch t(MUON_K_FINISH, stream);
+    if ((e = launch_finish(c, pl.totals[PH_FINISH], pl.bf16, fp)) != hipSuccess)
+      return hip_fail(e, "launch finish");
+    t.done();
+  }
+  return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" size_t muon_workspace_bytes(int32_t batch, const int64_t* rows, const int64_t* cols,
+                                       int32_t dtype) {
+  Plan pl;
+  if (make_plan(batch, rows, cols, dtype, pl) != MUON_OK) return SIZE_MAX;
+  return pl.total_bytes;
+}
+
+extern "C" int32_t muon_ns_batched(int32_t batch, const int64_t* rows, const int64_t* cols,
+                                   const void* const* x, void* const* out, int32_t dtype,
+                                   const muon_ns_params* p, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  try {
+    g_detail.clear();
+    Plan pl;
+    int32_t st = make_plan(batch, rows, cols, dtype, pl);
+    if (st != MUON_OK) return st;
+    if ((st = check_ns_params(p)) != MUON_OK) return st;
+    if (batch == 0) return MUON_OK;
+    if (x == nullptr || out == nullptr) return fail(MUON_ERR_INVALID_ARG, "x/out array is null");
+    for (int32_t i = 0; i < batch; ++i) {
+      if (x[i] == nullptr || out[i] == nullptr)
+        return fail(MUON_ERR_INVALID_ARG, "matrix %d: null device pointer", i);
+      if (!aligned16(x[i]) || !aligned16(out[i]))
+        return fail(MUON_ERR_INVALID_ARG, "matrix %d: device pointer not 16-byte aligned", i);
+    }
+    if ((st = check_ws(pl, workspace, workspace_bytes)) != MUON_OK) return st;
+    char* ws = static_cast<char*>(workspace);
+    bind(pl, ws);
+    for (int32_t i = 0; i < batch; ++i) {
+      pl.desc[i].src = x[i];
+      pl.desc[i].mom = nullptr;
+      pl.desc[i].dst = out[i];
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = upload_table(pl, ws, s)) != MUON_OK) return st;
+    ElemParams ep{};
+    ep.mode = MODE_NS;
+    ep.eps = p->eps;
+    return run(pl, ws, s, ep, *p);
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "unexpected host exception");
+  }
+}
+
+extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const int64_t* cols,
+                                     void* const* w, const void* const* g, void* const* m,
+                                     int32_t dtype, const muon_step_params* p, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  try {
+    g_detail.clear();
+    Plan pl;
+    int32_t st = make_plan(batch, rows, cols, dtype, pl);
+    if (st != MUON_OK) return st;
+    if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "params pointer is null");
+    if ((st = check_ns_params(&p->ns)) != MUON_OK) return st;
+    if (!std::isfinite(p->lr) || !std::isfinite(p->beta))
+      return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
+    if (p->nesterov != 0 && p->nesterov != 1)
+      return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
+    if (batch == 0) return MUON_OK;
+    if (w == nullptr || g == nullptr || m == nullptr)
+      return fail(MUON_ERR_INVALID_ARG, "w/g/m array is null");
+    for (int32_t i = 0; i < batch; ++i) {
+      if (w[i] == nullptr || g[i] == nullptr || m[i] == nullptr)
+        return fail(MUON_ERR_INVALID_ARG, "matrix %d: null device pointer", i);
+      if (!aligned16(w[i]) || !aligned16(g[i]) || !aligned16(m[i]))
+        return fail(MUON_ERR_INVALID_ARG, "matrix %d: device pointer not 16-byte aligned", i);
+      if (w[i] == g[i] || w[i] == m[i] || static_cast<const void*>(m[i]) == g[i])
+        return fail(MUON_ERR_INVALID_ARG, "matrix %d: w, g and m must be distinct buffers", i);
+    }
+    if ((st = check_ws(pl, workspace, workspace_bytes)) != MUON_OK) return st;
+    char* ws = static_cast<char*>(workspace);
+    bind(pl, ws);
+    for (int32_t i = 0; i < batch; ++i) {
+      pl.desc[i].src = g[i];
+      pl.desc[i].mom = m[i];
+      pl.desc[i].dst = w[i];
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = upload_table(pl, ws, s)) != MUON_OK) return st;
+    ElemParams ep{};
+    ep.mode = MODE_STEP;
+    ep.nesterov = p->nesterov;
+    ep.beta = p->beta;
+    ep.eps = p->ns.eps;
+    ep.lr = p->lr;
+    return run(pl, ws, s, ep, p->ns);
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "unexpected host exception");
+  }
+}
+
+extern "C" const char* muon_status_string(int32_t status) {
+  switch (status) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+    default: return "MUON_UNKNOWN_STATUS";
+  }
+}
+
+extern "C" const char* muon_last_error_detail(void) { return muon::g_detail.c_str(); }
+
+extern "C" int32_t muon_timing_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  g_timing_on = enable != 0;
+  return MUON_OK;
+}
+
+extern "C" int32_t muon_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  g_detail.clear();
+  if (kernel < 0 || kernel >= MUON_K_COUNT || total_ms == nullptr || launches == nullptr)
+    return fail(MUON_ERR_INVALID_ARG, "bad kernel id %d or null output", kernel);
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  const int32_t st = drain_timing();
+  if (st != MUON_OK) return st;
+  *total_ms = g_total_ms[kernel];
+  *launches = g_launches[kernel];
+  return MUON_OK;
+}
+
+extern "C" int32_t muon_timing_reset(void) {
+  g_detail.clear();
+  std::lock_guard<std::mutex> lock(g_timing_mu);
+  const int32_t st = drain_timing();
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    g_total_ms[k] = 0.0;
+    g_launches[k] = 0;
+  }
+  return st;
+}

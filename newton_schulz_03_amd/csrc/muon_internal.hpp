@@ -1,0 +1,71 @@
+// Internal definitions shared by the C ABI (host) and the kernels (device).
+//
+// Workspace layout, per call (offsets from the caller's 256-byte aligned base):
+//   [table]     MatDesc[batch], then the phase prefix arrays int32[NPHASE][batch+1]
+//   [partials]  float[reduce blocks]: per-block sums of squares (Frobenius norm)
+//   per matrix  X ping, X pong: s_pad x l_pad;  A (Gram), B (polynomial): s_pad x s_pad
+// Every matrix is held in its wide orientation (short side first): a matrix
+// with more rows than columns is transposed on the way in and back on the way
+// out.  s_pad and l_pad round the short and long sides up to the GEMM tile
+// (256); the padding holds zeros, which the iteration keeps at zero, so the
+// product kernels need no bounds checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kTile = 256;          // GEMM output tile (both sides) and padding granularity
+constexpr int kEwTile = 64;         // tile side of the normalize / finish kernels
+constexpr int kThreads = 256;       // threads per block, every kernel
+constexpr int kReduceIters = 8;     // 16-byte vectors per thread per reduce block
+constexpr int kAlign = 256;         // workspace sub-buffer alignment
+
+enum Phase : int { PH_REDUCE = 0, PH_NORMALIZE = 1, PH_SYM = 2, PH_PROD = 3, PH_FINISH = 4, NPHASE = 5 };
+enum Mode : int { MODE_NS = 0, MODE_STEP = 1 };
+
+struct MatDesc {
+  const void* src;   // NS: x;   STEP: g
+  void* mom;         // STEP: m (updated in place); NS: unused
+  void* dst;         // NS: out; STEP: w (updated in place)
+  void* x[2];        // ping-pong iterate, s_pad x l_pad, wide orientation
+  void* gram;        // A = X X^T, s_pad x s_pad
+  void* poly;        // B = b A + c A^2, s_pad x s_pad
+  int64_t rows, cols, numel;  // user shape
+  int32_t s, l;               // short and long side
+  int32_t s_pad, l_pad;
+  int32_t tall;               // rows > cols
+  int32_t vec_ok;             // cols is a multiple of the 16-byte vector width
+  float scale;                // sqrt(max(1, rows/cols))
+  int32_t reserved;
+};
+
+struct LaunchCtx {
+  const MatDesc* desc;     // device copy of the descriptors
+  const int32_t* prefix;   // device: NPHASE arrays of batch+1 block prefixes
+  float* partials;         // device: per reduce-block sums of squares
+  int32_t batch;
+  hipStream_t stream;
+};
+
+struct ElemParams {
+  int32_t mode;      // MODE_NS / MODE_STEP
+  int32_t nesterov;
+  float beta;
+  float eps;
+  float lr;
+  int32_t cur;       // which X buffer holds the final iterate (finish)
+};
+
+// Host launchers (one per kernel family).  is_bf16 selects the element type.
+hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
+hipError_t launch_normalize(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
+hipError_t launch_finish(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
+hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur);
+hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc);
+// X[next] = a * X[cur] + alpha * (Q X[cur]) with Q = B (use_poly) or A.
+hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur, float a,
+                       float alpha, bool use_poly);
+
+}  // namespace muon

@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI: exports, workspace sizing and validation.
+
+These run without a GPU.  Every call here fails validation (or is the batch = 0
+no-op) before the library touches the HIP runtime, so fake, aligned, never
+dereferenced pointer values are enough.
+"""
+import ctypes
+import re
+
+import pytest
+
+import newton_schulz_03_amd as nsa
+from newton_schulz_03_amd._binding import NsParams, StepParams, _i64_array, _ptr_array
+
+FAKE = 0x7f0000000000  # aligned, never dereferenced
+
+
+def header_functions():
+    text = open(nsa.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nsa.load_library()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = header_functions()
+    assert set(names) == set(nsa.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "MUON_OK"), (1, "MUON_ERR_INVALID_ARG"), (2, "MUON_ERR_UNSUPPORTED"),
+                       (3, "MUON_ERR_WORKSPACE"), (4, "MUON_ERR_HIP")]:
+        assert nsa.status_string(code) == name
+    assert nsa.status_string(99) == "MUON_UNKNOWN_STATUS"
+
+
+def expected_workspace(shapes, esize):
+    """Workspace layout restated from the header's description of the buffers."""
+    def up(x, a):
+        return (x + a - 1) // a * a
+
+    batch = len(shapes)
+    desc = 112  # sizeof(MatDesc)
+    total = up(desc * batch, 256) + up(4 * 5 * (batch + 1), 256)
+    vec = 16 // esize
+    blocks = sum(-(-r * c // (256 * vec * 8)) for r, c in shapes)
+    total += up(4 * blocks, 256)
+    for r, c in shapes:
+        s, l = min(r, c), max(r, c)
+        sp, lp = up(s, 256), up(l, 256)
+        total += 2 * up(sp * lp * esize, 256) + 2 * up(sp * sp * esize, 256)
+    return total
+
+
+@pytest.mark.parametrize("dtype,esize", [(nsa.MUON_BF16, 2), (nsa.MUON_FP32, 4)])
+def test_workspace_bytes(dtype, esize):
+    for shapes in [[(256, 512)], [(2048, 6144)] * 3, [(257, 771), (771, 257), (1, 5)],
+                   [(6144, 6144), (6144, 1024)]]:
+        assert nsa.workspace_bytes(shapes, dtype) == expected_workspace(shapes, esize)
+    assert nsa.workspace_bytes([], dtype) == 0
+
+
+def test_workspace_bytes_invalid(lib):
+    assert lib.muon_workspace_bytes(1, _i64_array([0]), _i64_array([5]), 0) == nsa._binding.SIZE_MAX
+    assert "shape" in nsa.last_error_detail()
+    assert lib.muon_workspace_bytes(1, _i64_array([5]), _i64_array([5]), 7) == nsa._binding.SIZE_MAX
+    assert lib.muon_workspace_bytes(-1, None, None, 0) == nsa._binding.SIZE_MAX
+
+
+def ns_call(lib, batch=1, rows=(64,), cols=(96,), x=(FAKE,), out=(FAKE + 4096,), dtype=0,
+            steps=5, coeffs=(3.4445, -4.775, 2.0315), eps=1e-7, ws=FAKE + (1 << 20),
+            ws_bytes=1 << 40, params=True):
+    p = NsParams(steps, *coeffs, eps)
+    return lib.muon_ns_batched(batch, _i64_array(rows) if rows is not None else None,
+                               _i64_array(cols) if cols is not None else None,
+                               _ptr_array(x) if x is not None else None,
+                               _ptr_array(out) if out is not None else None, dtype,
+                               ctypes.byref(p) if params else None, ctypes.c_void_p(ws),
+                               ws_bytes, None)
+
+
+def step_call(lib, w=FAKE, g=FAKE + 8192, m=FAKE + 16384, rows=(64,), cols=(96,), nesterov=0,
+              lr=0.02, beta=0.95, ws=FAKE + (1 << 20), ws_bytes=1 << 40, steps=5):
+    p = StepParams(lr, beta, nesterov, NsParams(steps, 3.4445, -4.775, 2.0315, 1e-7))
+    return lib.muon_step_batched(1, _i64_array(rows), _i64_array(cols), _ptr_array([w]),
+                                 _ptr_array([g]), _ptr_array([m]), 0, ctypes.byref(p),
+                                 ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_ns_validation(lib):
+    E = nsa
+    assert ns_call(lib, batch=0, rows=None, cols=None, x=None, out=None) == E.MUON_OK
+    assert ns_call(lib, batch=-1) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, rows=None) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, rows=(0,)) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, cols=(-3,)) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, rows=(E.MAX_DIM + 1,)) == E.MUON_ERR_UNSUPPORTED
+    assert ns_call(lib, dtype=2) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, steps=-1) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, params=False) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, coeffs=(float("nan"), 0.0, 0.0)) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, eps=-1.0) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, x=None) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, x=(0,)) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, out=(FAKE + 2,)) == E.MUON_ERR_INVALID_ARG
+    assert "aligned" in nsa.last_error_detail()
+    assert ns_call(lib, ws=0) == E.MUON_ERR_WORKSPACE
+    need = nsa.workspace_bytes([(64, 96)], 0)
+    assert ns_call(lib, ws_bytes=need - 1) == E.MUON_ERR_WORKSPACE
+    assert str(need) in nsa.last_error_detail()
+    assert ns_call(lib, ws=FAKE + 128) == E.MUON_ERR_INVALID_ARG
+
+
+def test_step_validation(lib):
+    E = nsa
+    assert step_call(lib, w=FAKE, g=FAKE) == E.MUON_ERR_INVALID_ARG  # aliasing
+    assert step_call(lib, m=FAKE + 8192) == E.MUON_ERR_INVALID_ARG
+    assert step_call(lib, nesterov=2) == E.MUON_ERR_INVALID_ARG
+    assert step_call(lib, lr=float("inf")) == E.MUON_ERR_INVALID_ARG
+    assert step_call(lib, steps=-2) == E.MUON_ERR_INVALID_ARG
+    assert step_call(lib, g=0) == E.MUON_ERR_INVALID_ARG
+    assert step_call(lib, ws_bytes=16) == E.MUON_ERR_WORKSPACE

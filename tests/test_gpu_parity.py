@@ -1,0 +1,221 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on the GPU.
+
+Sizes here finish in seconds on the oracle and still span several 256x256
+tiles with ragged tails, both orientations (wide and tall), square matrices,
+single rows and columns.  Full-size workloads are in test_gpu_fullsize.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import newton_schulz_03_amd as nsa
+import oracle
+import workloads
+from parity_util import TOL, device_inputs, host_f64, rel_fro, singular_values
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [(300, 700), (700, 300), (257, 771), (512, 512), (520, 1040), (1040, 520), (33, 65),
+          (1, 300), (300, 1), (1, 1), (97, 97), (256, 768)]
+
+
+def _wl(kind, dtype, shapes, **kw):
+    base = workloads.Workload(name="t", dtype=dtype, shapes=tuple(shapes),
+                              call="ns" if kind == "gauss" else "step", kind=kind, seed=77)
+    import dataclasses
+    return dataclasses.replace(base, **kw)
+
+
+def _ns_check(dtype, shapes, steps=5, coeffs=oracle.QUINTIC, tol=None, eps=1e-7):
+    wl = _wl("gauss", dtype, shapes, steps=steps, coeffs=coeffs)
+    ins = device_inputs(wl)
+    xs = [d["x"] for d in ins]
+    outs = nsa.ns_batched(xs, steps=steps, coeffs=coeffs, eps=eps)
+    torch.cuda.synchronize()
+    errs = []
+    for x, o in zip(xs, outs):
+        want = oracle.newton_schulz(host_f64(x), steps, coeffs, eps)
+        errs.append(rel_fro(host_f64(o), want))
+    tol = TOL[dtype] if tol is None else tol
+    assert max(errs) <= tol, list(zip(shapes, errs))
+    return errs
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.name}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def test_c1_fp32_quintic_and_band():
+    wl = workloads.standard_workloads()["c1_fp32_256x512"]
+    x = device_inputs(wl)[0]["x"]
+    o = nsa.ns_batched([x], steps=5)[0]
+    want = oracle.newton_schulz(host_f64(x), 5)
+    assert rel_fro(host_f64(o), want) <= TOL["fp32"]
+    sv = singular_values(host_f64(o))
+    assert 0.6818 <= sv.min() and sv.max() <= 1.1344
+
+
+def test_c1_fp32_cubic30_polar():
+    import scipy.linalg
+
+    wl = workloads.c1_cubic()
+    x = device_inputs(wl)[0]["x"]
+    o = nsa.ns_batched([x], steps=30, coeffs=oracle.CUBIC)[0]
+    xh = host_f64(x)
+    assert rel_fro(host_f64(o), oracle.newton_schulz(xh, 30, oracle.CUBIC)) <= TOL["fp32"]
+    assert rel_fro(host_f64(o), scipy.linalg.polar(xh)[0]) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ns_ragged_batch(dtype):
+    _ns_check(dtype, RAGGED)
+
+
+@pytest.mark.parametrize("coeffs,steps", [((1.0, 0.0, 0.0), 1), ((0.0, 1.0, 0.0), 1),
+                                          ((0.0, 0.0, 1.0), 1), ((0.5, 0.25, -0.125), 2),
+                                          (oracle.QUINTIC, 0)])
+def test_ns_pieces_fp32(coeffs, steps):
+    """Gram, polynomial and product in isolation: X, A X, A^2 X, and steps = 0 (X0)."""
+    _ns_check("fp32", [(300, 700), (700, 300), (512, 512)], steps=steps, coeffs=coeffs, tol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ns_cubic_skips_square(dtype):
+    _ns_check(dtype, [(300, 700), (700, 300)], steps=8, coeffs=oracle.CUBIC)
+
+
+@pytest.mark.parametrize("dtype,nesterov", [("bf16", False), ("bf16", True), ("fp32", False),
+                                            ("fp32", True)])
+def test_step_parity(dtype, nesterov):
+    shapes = [(300, 700), (700, 300), (256, 768), (513, 257)]
+    wl = _wl("muon", dtype, shapes, nesterov=nesterov)
+    ins = device_inputs(wl)
+    w = [d["w"] for d in ins]
+    g = [d["g"] for d in ins]
+    m = [d["m"] for d in ins]
+    w0 = [host_f64(t) for t in w]
+    g0 = [host_f64(t) for t in g]
+    m0 = [host_f64(t) for t in m]
+    nsa.step_batched(w, g, m, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5)
+    torch.cuda.synchronize()
+    # orthogonalized update of the GPU's own U, through the orthogonalize-only entry point
+    us = [(gi.float() + wl.beta * mi.float()).to(gi.dtype) if nesterov else mi.clone()
+          for gi, mi in zip(g, m)]
+    o_gpu = nsa.ns_batched(us, steps=5)
+    torch.cuda.synchronize()
+    for i, (r, c) in enumerate(shapes):
+        w_ref, m_ref, o_ref = oracle.muon_step(w0[i], g0[i], m0[i], lr=wl.lr, beta=wl.beta,
+                                               nesterov=nesterov, steps=5)
+        assert rel_fro(host_f64(m[i]), m_ref) <= TOL[dtype] / 4
+        assert rel_fro(host_f64(o_gpu[i]), o_ref) <= TOL[dtype]
+        # W' is the stored rounding of W - lr*scale*O evaluated in fp32: within one ulp of
+        # the result, plus fp32 evaluation error relative to the operands (lr and the
+        # product are rounded to fp32, which matters where W and lr*scale*O cancel)
+        scale = math.sqrt(max(1.0, r / c))
+        upd = wl.lr * scale * host_f64(o_gpu[i])
+        expect = w0[i] - upd
+        got = host_f64(w[i])
+        ulp = np.spacing(np.maximum(np.abs(expect), np.abs(got)).astype(np.float32)).astype(np.float64)
+        if dtype == "bf16":
+            ulp = ulp * 2.0 ** 16
+        bound = ulp + 4.0 * 2.0 ** -24 * (np.abs(w0[i]) + np.abs(upd))
+        if nesterov:
+            # the step forms U = G + beta*M' in fp32, the reference above from U rounded to
+            # the dtype: allow for that difference in O (a few times its expected size)
+            rms_o = float(np.sqrt(np.mean(host_f64(o_gpu[i]) ** 2)))
+            bound = bound + wl.lr * scale * 8.0 * TOL[dtype] * rms_o
+        assert np.all(np.abs(got - expect) <= bound), (r, c, float(np.max(np.abs(got - expect) / bound)))
+        # the update itself against the oracle's lr*scale*O; in bf16 the stored W'
+        # quantizes an update of about two ulps of W, hence the loose bf16 bound
+        assert rel_fro(w0[i] - got, w0[i] - w_ref) <= (TOL[dtype] if dtype == "fp32" else 0.3)
+
+
+def test_determinism_bitwise():
+    wl = _wl("muon", "bf16", [(300, 700), (700, 300), (512, 512)])
+    ins = device_inputs(wl)
+    runs = []
+    for _ in range(2):
+        w = [d["w"].clone() for d in ins]
+        m = [d["m"].clone() for d in ins]
+        nsa.step_batched(w, [d["g"] for d in ins], m)
+        torch.cuda.synchronize()
+        runs.append([t.view(torch.int16).cpu() for t in w + m])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
+
+
+def test_resume_from_saved_momentum():
+    """Two steps equal one step, a save/restore of (W, M), and a second step."""
+    wl = _wl("muon", "bf16", [(300, 700), (700, 300)])
+    ins = device_inputs(wl)
+    g = [d["g"] for d in ins]
+    w1 = [d["w"].clone() for d in ins]
+    m1 = [d["m"].clone() for d in ins]
+    nsa.step_batched(w1, g, m1)
+    nsa.step_batched(w1, g, m1)
+    w2 = [d["w"].clone() for d in ins]
+    m2 = [d["m"].clone() for d in ins]
+    nsa.step_batched(w2, g, m2)
+    saved = [t.cpu() for t in w2 + m2]
+    w3 = [t.to("cuda") for t in saved[:2]]
+    m3 = [t.to("cuda") for t in saved[2:]]
+    nsa.step_batched(w3, g, m3)
+    torch.cuda.synchronize()
+    for a, b in zip(w1 + m1, w3 + m3):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_zero_and_inplace_and_nan():
+    torch.manual_seed(1234)
+    x = torch.zeros(300, 700, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn(260, 300, device="cuda").to(torch.bfloat16)
+    z = torch.randn(64, 128, device="cuda").to(torch.bfloat16)
+    z[3, 5] = float("nan")
+    y_host = host_f64(y)
+    outs = nsa.ns_batched([x, y, z], out=[x, y, z.clone()])  # x and y in place
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(outs[0]) == 0
+    assert rel_fro(host_f64(outs[1]), oracle.newton_schulz(y_host, 5)) <= TOL["bf16"]
+    assert torch.isnan(outs[2]).all()
+    # zero gradient and momentum: zero update
+    w = torch.randn(300, 700, device="cuda").to(torch.bfloat16)
+    w0 = w.clone()
+    g = torch.zeros_like(w)
+    m = torch.zeros_like(w)
+    nsa.step_batched([w], [g], [m])
+    torch.cuda.synchronize()
+    assert torch.equal(w.view(torch.int16), w0.view(torch.int16))
+
+
+def test_validation_enqueues_nothing():
+    x = torch.randn(300, 700, device="cuda").to(torch.bfloat16)
+    out = torch.full_like(x, 7.0)
+    ws = nsa.allocate_workspace([(300, 700)], torch.bfloat16, "cuda")
+    small = ws[: ws.numel() // 2]
+    with pytest.raises(nsa.MuonError) as e:
+        nsa.ns_batched([x], out=[out], workspace=small)
+    assert e.value.status == nsa.MUON_ERR_WORKSPACE
+    with pytest.raises(nsa.MuonError) as e:
+        nsa.ns_batched([x], out=[out], steps=-1, workspace=ws)
+    assert e.value.status == nsa.MUON_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+
+
+def test_workspace_reuse_across_shapes():
+    """A workspace sized for a large batch serves a smaller one; results match fresh runs."""
+    big = [(700, 300), (520, 1040)]
+    ws = nsa.allocate_workspace(big, torch.bfloat16, "cuda")
+    wl = _wl("gauss", "bf16", big)
+    xs = [d["x"] for d in device_inputs(wl)]
+    a = nsa.ns_batched(xs, workspace=ws)
+    b = nsa.ns_batched(xs[:1], workspace=ws)
+    c = nsa.ns_batched(xs[:1])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(b[0].view(torch.int16), c[0].view(torch.int16))
