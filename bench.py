@@ -103,6 +103,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="c2_96x2048x6144")
     ap.add_argument("--cpu-sample", type=int, default=2, help="matrices timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (a known "
+                         "byte count for scaling hardware traffic counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -219,6 +222,15 @@ def main(argv=None) -> int:
         "ns_kernels_ms_per_step": round(ns_ms, 3),
         "kernels": per_kernel,
     }
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        result["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         print(f"[bench] timing the oracle on {args.cpu_sample} matrices", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)

@@ -1,5 +1,6 @@
-// Matrix-core kernels of the Newton-Schulz iteration, on the padded wide
-// iterate X (s_pad x l_pad, row-major):
+// Matrix-core kernels of the Newton-Schulz iteration, fp32 mode, on the padded
+// wide iterate X (s_pad x l_pad, row-major).  (bf16 runs the pipelined kernel
+// of gemm_bf16.hip; the tile decode and epilogues are shared.)
 //   GRAM  A = X X^T          upper-triangle tiles only, each stored twice (mirror)
 //   POLY  B = b A + c A A    A is symmetric, so A A = A A^T: same form as GRAM
 //   PROD  X' = a X + alpha Q X   with Q = B (or A when c == 0)
@@ -14,7 +15,7 @@
 // transposed in registers on the way into LDS.  LDS rows are XOR-swizzled in
 // 16-byte chunks so that both the row-wise fills and the fragment reads spread
 // over the banks.
-#include "device_common.hpp"
+#include "gemm_common.hpp"
 
 namespace muon {
 
@@ -25,8 +26,6 @@ constexpr int kRowsPerOp = kTile;              // 256 rows per operand
 constexpr int kOpBytes = kRowsPerOp * kRowBytes;  // 32 KiB
 constexpr int kStageBytes = 2 * kOpBytes;         // P and Q operands
 constexpr int kLdsBytes = 2 * kStageBytes;        // two stages: 128 KiB
-
-enum GemmMode : int { GM_GRAM = 0, GM_POLY = 1, GM_PROD = 2 };
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
@@ -116,72 +115,18 @@ __device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const u32x4_t& p, cons
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void load4(const T* p, float* v) {
-  if constexpr (sizeof(T) == 2) {
-    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
-    v[0] = __uint_as_float(w[0] << 16);
-    v[1] = __uint_as_float(w[0] & 0xffff0000u);
-    v[2] = __uint_as_float(w[1] << 16);
-    v[3] = __uint_as_float(w[1] & 0xffff0000u);
-  } else {
-    const u32x4_t w = ld16(p);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(w[e]);
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void store4(T* p, const float* v) {
-  if constexpr (sizeof(T) == 2) {
-    u32x2_t w;
-    w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[0])) |
-           (static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[1])) << 16);
-    w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[2])) |
-           (static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[3])) << 16);
-    *reinterpret_cast<u32x2_t*>(p) = w;
-  } else {
-    u32x4_t w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(v[e]);
-    st16(p, w);
-  }
-}
-
-// Upper-triangle tile (ti <= tj) number t of a T x T tile grid, row by row.
-__device__ __forceinline__ void sym_tile(int32_t t, int32_t T, int32_t& ti, int32_t& tj) {
-  int32_t i = 0;
-  while (t >= T - i) {
-    t -= T - i;
-    ++i;
-  }
-  ti = i;
-  tj = i + t;
-}
-
 }  // namespace
 
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(LaunchCtx c, int32_t cur, float a,
-                                                      float alpha, float beta_c, int32_t use_poly) {
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   constexpr int BK = kRowBytes / sizeof(T);
 
-  const int32_t b = xcd_remap(static_cast<int32_t>(blockIdx.x), static_cast<int32_t>(gridDim.x));
-  const int32_t* pre = c.prefix + (MODE == GM_PROD ? PH_PROD : PH_SYM) * (c.batch + 1);
-  const int j = find_matrix(pre, c.batch, b);
-  const MatDesc& d = c.desc[j];
-  const int32_t t = b - pre[j];
-  const int32_t ts = d.s_pad / kTile;
-  int32_t ti, tj;
-  if constexpr (MODE == GM_PROD) {
-    ti = t % ts;  // tile row along the short side, fastest: neighbours share X columns
-    tj = t / ts;
-  } else {
-    sym_tile(t, ts, ti, tj);
-  }
+  const TileRef tr = decode_tile<MODE>(c);
+  const MatDesc& d = tr.d;
+  const int32_t ti = tr.ti, tj = tr.tj;
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
-  const T* Xc = static_cast<const T*>(d.x[cur]);
+  const T* Xc = static_cast<const T*>(d.x[g.cur]);
 
   // Operand P (MFMA rows, index p) and Q (MFMA columns, index q): D[p][q] = sum_k P[p][k] Q[q][k].
   const T* p_base;
@@ -198,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(LaunchCtx c, int32_t cur, 
     K = s_pad;
   } else {
     // P = columns tj of X (transposed on the way into LDS), Q = rows ti of B (or A)
-    const T* Q = static_cast<const T*>(use_poly ? d.poly : d.gram);
+    const T* Q = static_cast<const T*>(g.use_poly ? d.poly : d.gram);
     p_base = Xc + tj * kTile;  p_ld = l_pad;
     q_base = Q + ti * kTile * s_pad;  q_ld = s_pad;
     K = s_pad;
@@ -213,12 +158,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(LaunchCtx c, int32_t cur, 
   const int lr = lane & 31, lh = lane >> 5;
 
   f32x16_t acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+  zero_acc(acc);
 
   const int nk = static_cast<int>(K / BK);
   pt.load(p_base, p_ld, 0);
@@ -256,86 +196,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(LaunchCtx c, int32_t cur, 
     }
     __syncthreads();
   }
-
-  // Epilogue.  Lane (lr, lh) holds D[p0 + e][q] for e = 0..3, with
-  // p0 = wm*128 + mi*32 + 8g + 4lh and q = wn*128 + ni*32 + lr, in acc[mi][ni][4g + e].
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int p0 = wm * 128 + mi * 32 + 8 * g + 4 * lh;
-        const int q = wn * 128 + ni * 32 + lr;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[mi][ni][4 * g + e];
-        if constexpr (MODE == GM_PROD) {
-          // D[p][q] = (Q X)[ti*256 + q][tj*256 + p]
-          const int64_t row = static_cast<int64_t>(ti) * kTile + q;
-          const int64_t col = static_cast<int64_t>(tj) * kTile + p0;
-          float x[4];
-          load4<T>(Xc + row * l_pad + col, x);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = a * x[e] + alpha * v[e];
-          store4<T>(static_cast<T*>(d.x[cur ^ 1]) + row * l_pad + col, v);
-        } else {
-          T* out = static_cast<T*>(MODE == GM_GRAM ? d.gram : d.poly);
-          const int64_t rq = static_cast<int64_t>(tj) * kTile + q;   // mirror row
-          const int64_t cp = static_cast<int64_t>(ti) * kTile + p0;  // mirror col
-          if constexpr (MODE == GM_POLY) {
-            // A[ti*256+p][tj*256+q] = A[tj*256+q][ti*256+p]: A is stored symmetric
-            float av[4];
-            load4<T>(static_cast<const T*>(d.gram) + rq * s_pad + cp, av);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = alpha * av[e] + beta_c * v[e];
-          }
-          float r[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = Elt<T>::to_f32(Elt<T>::from_f32(v[e]));
-          store4<T>(out + rq * s_pad + cp, r);
-          if (ti != tj) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[(cp + e) * s_pad + rq] = Elt<T>::from_f32(r[e]);
-          }
-        }
-      }
-    }
-  }
+  gemm_store<T, MODE, true>(acc, tr, g);
 }
 
-hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur) {
+namespace {
+
+template <int MODE>
+hipError_t launch_mode(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const GemmArgs& g) {
   if (nblocks <= 0) return hipSuccess;
-  if (is_bf16)
-    hipLaunchKernelGGL((k_gemm<uint16_t, GM_GRAM>), dim3(nblocks), dim3(kThreads), 0, c.stream, c,
-                       cur, 0.f, 0.f, 0.f, 0);
-  else
-    hipLaunchKernelGGL((k_gemm<float, GM_GRAM>), dim3(nblocks), dim3(kThreads), 0, c.stream, c, cur,
-                       0.f, 0.f, 0.f, 0);
+  if (is_bf16) return launch_gemm_bf16(MODE, c, nblocks, g);
+  hipLaunchKernelGGL((k_gemm_staged<float, MODE>), dim3(nblocks), dim3(kThreads), 0, c.stream, c,
+                     g);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
+                       float out_scale) {
+  GemmArgs g{cur, 0.f, out_scale, 0};
+  return launch_mode<GM_GRAM>(c, nblocks, is_bf16, g);
 }
 
 hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc) {
-  if (nblocks <= 0) return hipSuccess;
-  if (is_bf16)
-    hipLaunchKernelGGL((k_gemm<uint16_t, GM_POLY>), dim3(nblocks), dim3(kThreads), 0, c.stream, c,
-                       0, 0.f, b, cc, 0);
-  else
-    hipLaunchKernelGGL((k_gemm<float, GM_POLY>), dim3(nblocks), dim3(kThreads), 0, c.stream, c, 0,
-                       0.f, b, cc, 0);
-  return hipGetLastError();
+  GemmArgs g{0, b / cc, cc, 0};
+  return launch_mode<GM_POLY>(c, nblocks, is_bf16, g);
 }
 
 hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur, float a,
-                       float alpha, bool use_poly) {
-  if (nblocks <= 0) return hipSuccess;
-  if (is_bf16)
-    hipLaunchKernelGGL((k_gemm<uint16_t, GM_PROD>), dim3(nblocks), dim3(kThreads), 0, c.stream, c,
-                       cur, a, alpha, 0.f, use_poly ? 1 : 0);
-  else
-    hipLaunchKernelGGL((k_gemm<float, GM_PROD>), dim3(nblocks), dim3(kThreads), 0, c.stream, c, cur,
-                       a, alpha, 0.f, use_poly ? 1 : 0);
-  return hipGetLastError();
+                       bool use_poly) {
+  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0};
+  return launch_mode<GM_PROD>(c, nblocks, is_bf16, g);
 }
 
 }  // namespace muon

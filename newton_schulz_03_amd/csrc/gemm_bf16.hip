@@ -1,0 +1,455 @@
+// Pipelined bf16 matrix-core kernel of the Newton-Schulz iteration (gfx950).
+//
+// Same three products and tile layout as the fp32 path (see gemm_common.hpp);
+// what differs is how operands reach the matrix cores:
+//
+//  * Global -> LDS without registers: buffer_load_dwordx4 ... lds writes each
+//    lane's 16 bytes straight into LDS (lane i at base + 16 i).  The LDS layout
+//    is therefore chosen by permuting which global chunk each lane fetches.
+//  * A ring of 4 LDS stages of 32 K-values (P and Q tiles of 256 x 32 bf16,
+//    32 KiB per stage, 128 KiB in all): k-slice j is requested three slices
+//    before it is consumed, and one barrier per slice suffices.
+//  * K-major operands (rows of X, A or B) are kept as 64-byte rows, their four
+//    16-byte chunks XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3 so that the
+//    fragment reads (8 consecutive rows per 128 bytes of banks) do not collide.
+//  * The MN-major operand of the product (X read along its columns) stays in
+//    its natural layout, [k][n] with 512-byte rows, chunks swizzled by
+//    2 (k & 3); fragments are assembled with ds_read_b64_tr_b16, whose 16-lane
+//    groups read a 4 x 16 block and hand each lane one column.
+//  * Fragments are software-pipelined across the slice boundary: the reads of
+//    the next slice's first half overlap the MFMAs of this slice's second half.
+#include "gemm_common.hpp"
+
+namespace muon {
+
+namespace {
+
+constexpr int BK = 32;                      // K values per stage
+constexpr int KROW = BK * 2;                // bytes of one K-major LDS row
+constexpr int OPB = kTile * KROW;           // 16 KiB per operand per stage
+constexpr int STAGEB = 2 * OPB;             // P then Q
+constexpr int NST = 4;                      // stages in the ring
+constexpr int LDSB = NST * STAGEB;          // 128 KiB
+constexpr int LPO = OPB / (kThreads * 16);  // 16-byte loads per thread, operand and stage (4)
+constexpr int MNROW = kTile * 2;            // bytes of one MN-major LDS row (256 columns)
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int kkey(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// s_waitcnt on vmcnt only (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+// One 16-byte-per-lane load straight into LDS: lane i's data lands at
+// lds_addr + 16 i.  Written as inline assembly so that the compiler does not
+// guard every later LDS read with a full vmcnt wait; the kernel waits on vmcnt
+// itself, counting the loads it has in flight.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, int32_t voff, i32x4_t rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// One operand's stream of 256 x 32 tiles into the LDS ring.
+struct Stream {
+  const char* base;     // byte address of the operand tile at k-slice 0 (uniform)
+  int64_t step;         // bytes the base advances per k-slice
+  int64_t extent;       // bytes addressable from base at k-slice 0
+  int32_t voff[LPO];    // per-lane byte offsets, one per load instruction
+  int32_t lds;          // LDS byte offset of this wave's first 1 KiB block, within the operand
+
+  // Buffer resource for k-slice ks: base, stride 0, num_records (bytes), raw dword access.
+  __device__ __forceinline__ i32x4_t rsrc(int ks) const {
+    const uint64_t b = reinterpret_cast<uint64_t>(base) + static_cast<uint64_t>(ks) * step;
+    const int64_t left = extent - static_cast<int64_t>(ks) * step;
+    i32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(b & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((b >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(
+        static_cast<int32_t>(left > 0x7fffffffLL ? 0x7fffffffLL : (left < 0 ? 0 : left)));
+    r[3] = 0x00020000;
+    return r;
+  }
+  __device__ __forceinline__ void issue_one(int ks, uint32_t stage_op_lds, int u) const {
+    lds_dma16(__builtin_amdgcn_readfirstlane(stage_op_lds + lds + u * 1024), voff[u], rsrc(ks));
+  }
+  __device__ __forceinline__ void issue(int ks, uint32_t stage_op_lds) const {
+    const i32x4_t r = rsrc(ks);
+#pragma unroll
+    for (int u = 0; u < LPO; ++u)
+      lds_dma16(__builtin_amdgcn_readfirstlane(stage_op_lds + lds + u * 1024), voff[u], r);
+  }
+};
+
+// Rows [row0, row0+256) of a row-major matrix (leading dimension ld), K along the row.
+__device__ __forceinline__ Stream kmajor_stream(const uint16_t* m, int64_t row0, int64_t ld,
+                                                int64_t K, int wave, int lane) {
+  Stream s;
+  s.base = reinterpret_cast<const char*>(m + row0 * ld);
+  s.step = KROW;
+  s.extent = (255 * ld + K) * 2;
+#pragma unroll
+  for (int u = 0; u < LPO; ++u) {
+    const int row = 16 * (LPO * wave + u) + (lane >> 2);
+    const int c = (lane & 3) ^ kkey(row);
+    s.voff[u] = static_cast<int32_t>(row * ld * 2 + c * 16);
+  }
+  s.lds = LPO * wave * 1024;
+  return s;
+}
+
+// Columns [n0, n0+256) of a row-major matrix with K rows, K along the column.
+__device__ __forceinline__ Stream mnmajor_stream(const uint16_t* m, int64_t n0, int64_t ld,
+                                                 int64_t K, int wave, int lane) {
+  Stream s;
+  s.base = reinterpret_cast<const char*>(m + n0);
+  s.step = static_cast<int64_t>(BK) * ld * 2;
+  s.extent = ((K - 1) * ld + kTile) * 2;
+#pragma unroll
+  for (int u = 0; u < LPO; ++u) {
+    const int k = 2 * (LPO * wave + u) + (lane >> 5);
+    const int c = (lane & 31) ^ (2 * (k & 3));
+    s.voff[u] = static_cast<int32_t>(k * ld * 2 + c * 16);
+  }
+  s.lds = LPO * wave * 1024;
+  return s;
+}
+
+struct Frags {
+  u32x4_t p[4];
+  u32x4_t q[4];
+};
+
+__device__ __forceinline__ u32x4_t lds16(const char* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ u32x4_t lds_tr(const char* p0, const char* p1) {
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(p0));
+  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(p1));
+  const u32x2_t ua = __builtin_bit_cast(u32x2_t, a), ub = __builtin_bit_cast(u32x2_t, b);
+  u32x4_t r;
+  r[0] = ua[0];
+  r[1] = ua[1];
+  r[2] = ub[0];
+  r[3] = ub[1];
+  return r;
+}
+
+// Stores the finished tile through LDS (the ring is idle once the K loop is
+// done), so that global writes are whole 16-byte pieces of rows.
+//   Tile T (256 x 256 bf16, 128 KiB) is laid out as rows of 512 bytes, row
+//   index = the accumulator's q, 16-byte chunk c stored at c ^ (q & 31).
+//   PROD       T[q][p] = X'[ti*256 + q][tj*256 + p]: rows go out as they are.
+//   GRAM/POLY  T[q][p] = S[tj*256 + q][ti*256 + p] (the mirror); rows go out to
+//              the mirror position, and for ti != tj the columns of T, read with
+//              ds_read_b64_tr_b16, go out as rows of S[ti*256 + p][tj*256 + q].
+template <int MODE>
+__device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], const TileRef& tr,
+                                               const GemmArgs& g, char* smem, int wave,
+                                               int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  const float scale = MODE == GM_PROD ? 1.f : g.out_scale;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int q = wn * 128 + ni * 32 + lr;
+        const int c = 16 * wm + 4 * mi + gg;  // chunk of p0 = wm*128 + mi*32 + 8gg (+4lh)
+        u32x2_t w;
+        w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 0])) |
+               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 1])) << 16);
+        w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 2])) |
+               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 3])) << 16);
+        *reinterpret_cast<u32x2_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4) + 8 * lh) = w;
+      }
+  __syncthreads();
+  const int t = threadIdx.x;
+  // Rows of T: thread t moves chunk (t & 31) of rows (t >> 5) + 8u.
+  {
+    uint16_t* dst;
+    int64_t ld, r0, c0;
+    if constexpr (MODE == GM_PROD) {
+      dst = static_cast<uint16_t*>(tr.d.x[g.cur ^ 1]);
+      ld = tr.d.l_pad;
+      r0 = static_cast<int64_t>(tr.ti) * kTile;
+      c0 = static_cast<int64_t>(tr.tj) * kTile;
+    } else {
+      dst = static_cast<uint16_t*>(MODE == GM_GRAM ? tr.d.gram : tr.d.poly);
+      ld = tr.d.s_pad;
+      r0 = static_cast<int64_t>(tr.tj) * kTile;
+      c0 = static_cast<int64_t>(tr.ti) * kTile;
+    }
+    const int c = t & 31;
+#pragma unroll 8
+    for (int u = 0; u < 32; ++u) {
+      const int q = (t >> 5) + 8 * u;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4));
+      st16(dst + (r0 + q) * ld + c0 + 8 * c, v);
+    }
+  }
+  if constexpr (MODE != GM_PROD) {
+    if (tr.ti != tr.tj) {
+      // Columns of T.  Wave instruction I = 32 wave + u covers p-block pb = I / 8
+      // (16 columns) and q-chunks 4 (I % 8) + group; each lane gets 8 consecutive q
+      // of one column p from two transposed reads.
+      uint16_t* dst = static_cast<uint16_t*>(MODE == GM_GRAM ? tr.d.gram : tr.d.poly);
+      const int64_t ld = tr.d.s_pad;
+      const int64_t r0 = static_cast<int64_t>(tr.ti) * kTile;
+      const int64_t c0 = static_cast<int64_t>(tr.tj) * kTile;
+      const int grp = lane >> 4, j = lane & 15;
+      const int r = (lane >> 2) & 3, qq = lane & 3;
+#pragma unroll 4
+      for (int u = 0; u < 32; ++u) {
+        const int I = 32 * wave + u;
+        const int pb = I >> 3, cq = 4 * (I & 7) + grp;
+        u32x4_t v;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 8 * cq + 4 * h + r;
+          const int chunk = 2 * pb + (qq >> 1);
+          const char* a = smem + row * MNROW + ((chunk ^ (row & 31)) << 4) + 8 * (qq & 1);
+          const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a));
+          const u32x2_t xu = __builtin_bit_cast(u32x2_t, x);
+          v[2 * h] = xu[0];
+          v[2 * h + 1] = xu[1];
+        }
+        st16(dst + (r0 + 16 * pb + j) * ld + c0 + 8 * cq, v);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDSB];
+
+  const TileRef tr = decode_tile<MODE>(c);
+  const MatDesc& d = tr.d;
+  const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
+  const uint16_t* Xc = static_cast<const uint16_t*>(d.x[g.cur]);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  Stream sp, sq;
+  int64_t K;
+  if constexpr (MODE == GM_GRAM) {
+    K = l_pad;
+    sp = kmajor_stream(Xc, static_cast<int64_t>(tr.ti) * kTile, l_pad, K, wave, lane);
+    sq = kmajor_stream(Xc, static_cast<int64_t>(tr.tj) * kTile, l_pad, K, wave, lane);
+  } else if constexpr (MODE == GM_POLY) {
+    K = s_pad;
+    const uint16_t* A = static_cast<const uint16_t*>(d.gram);
+    sp = kmajor_stream(A, static_cast<int64_t>(tr.ti) * kTile, s_pad, K, wave, lane);
+    sq = kmajor_stream(A, static_cast<int64_t>(tr.tj) * kTile, s_pad, K, wave, lane);
+  } else {
+    K = s_pad;
+    const uint16_t* Q = static_cast<const uint16_t*>(g.use_poly ? d.poly : d.gram);
+    sp = mnmajor_stream(Xc, static_cast<int64_t>(tr.tj) * kTile, l_pad, K, wave, lane);
+    sq = kmajor_stream(Q, static_cast<int64_t>(tr.ti) * kTile, s_pad, K, wave, lane);
+  }
+  const int nk = static_cast<int>(K / BK);
+
+  // Per-lane fragment offsets within a stage.
+  //  K-major: row (base + 32x + lr), chunk (2 sub + lh) ^ kkey(lr)   [kkey(base + 32x + lr) = kkey(lr)]
+  int32_t qoff[2], poff[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int sw = ((2 * sub + lh) ^ kkey(lr)) << 4;
+    qoff[sub] = OPB + (wn * 128 + lr) * KROW + sw;
+    poff[sub] = (wm * 128 + lr) * KROW + sw;
+  }
+  //  MN-major (product): 16-lane group gq, source row r, column quad qq
+  int32_t moff[4];
+  {
+    const int gq = lane >> 4, r = (lane >> 2) & 3, qq = lane & 3;
+    const int t0 = (8 * (gq >> 1) + r) * MNROW + 8 * (qq & 1);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      moff[mi] = t0 + ((((16 * wm + 4 * mi + 2 * (gq & 1) + (qq >> 1))) ^ (2 * r)) << 4);
+  }
+
+  // Fragment reads, numbered in the order the MFMAs below consume them:
+  // P[0] first (two transposed halves in the product), then Q[0..3], then P[1..3].
+  constexpr int NREAD = MODE == GM_PROD ? 12 : 8;
+  auto read_op = [&](Frags& f, const char* stage, int sub, int i) {
+    if constexpr (MODE == GM_PROD) {
+      if (i < 2) {
+        const char* base = stage + moff[0] + 16 * sub * MNROW + 4 * i * MNROW;
+        const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(base));
+        const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
+        f.p[0][2 * i] = u[0];
+        f.p[0][2 * i + 1] = u[1];
+      } else if (i < 6) {
+        f.q[i - 2] = lds16(stage + qoff[sub] + (i - 2) * 32 * KROW);
+      } else {
+        const int mi = 1 + (i - 6) / 2, h = (i - 6) % 2;
+        const char* base = stage + moff[mi] + 16 * sub * MNROW + 4 * h * MNROW;
+        const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(base));
+        const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
+        f.p[mi][2 * h] = u[0];
+        f.p[mi][2 * h + 1] = u[1];
+      }
+    } else {
+      if (i == 0) {
+        f.p[0] = lds16(stage + poff[sub]);
+      } else if (i < 5) {
+        f.q[i - 1] = lds16(stage + qoff[sub] + (i - 1) * 32 * KROW);
+      } else {
+        f.p[i - 4] = lds16(stage + poff[sub] + (i - 4) * 32 * KROW);
+      }
+    }
+  };
+
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+
+  // The s-multiple of the source tile (PROD: a X; POLY: (b/c) A) comes from the
+  // matrix cores.  In the slice that streams the needed rows, the fragments
+  // already in registers times a scaled identity give exactly that term:
+  //   PROD  sum_k X[32kt+k][p] * (s d(q,k))  = s X[32kt+q][p]   (identity as the Q operand)
+  //   POLY  sum_k (s d(p,k)) * A[tj*256+q][32kt+k] = s A[ti*256+p][tj*256+q]   (as P)
+  // s is split into bf16 hi + lo parts, so the term is exact to ~1e-5.  The
+  // identity fragment of K-half h: lane l, element e is nonzero iff
+  // (l & 31) == 16h + 8(l >> 5) + e.
+  const __bf16 s_hi = static_cast<__bf16>(g.init_scale);
+  const __bf16 s_lo = static_cast<__bf16>(g.init_scale - static_cast<float>(s_hi));
+  auto ident = [&](int h, __bf16 v) {
+    bf16x8_t r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = lr == 16 * h + 8 * lh + e ? v : static_cast<__bf16>(0.f);
+    return r;
+  };
+  // Term MFMAs for block R of this wave (R is a compile-time constant; -1: none).
+  auto term_op = [&](const Frags& f, int h, auto R) {
+    constexpr int r = decltype(R)::value;
+    if constexpr (MODE != GM_GRAM && r >= 0) {
+      const bf16x8_t id[2] = {ident(h, s_hi), ident(h, s_lo)};
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          if constexpr (MODE == GM_PROD)
+            acc[x][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, f.p[x]), id[part], acc[x][r], 0, 0, 0);
+          else
+            acc[r][x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                id[part], __builtin_bit_cast(bf16x8_t, f.q[x]), acc[r][x], 0, 0, 0);
+        }
+    }
+  };
+
+  auto mfma_op = [&](const Frags& f, int i) {
+    const int mi = i >> 2, ni = i & 3;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, f.p[mi]),
+                                                          __builtin_bit_cast(bf16x8_t, f.q[ni]),
+                                                          acc[mi][ni], 0, 0, 0);
+  };
+
+  // LDS byte address of the ring (the low 32 bits of an LDS pointer are its offset).
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)smem));
+
+  // Prologue: request slices 0..NST-1, wait for slice 0.  Slice indices past the
+  // end are clamped to the last slice: the extra loads refill a stage nobody
+  // reads again and keep the count of loads in flight the same every iteration.
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+    const int ks = s < nk ? s : nk - 1;
+    sp.issue(ks, ring + s * STAGEB);
+    sq.issue(ks, ring + s * STAGEB + OPB);
+  }
+  wait_vm<(NST - 1) * 2 * LPO>();
+  __syncthreads();
+
+  Frags f0, f1;
+#pragma unroll
+  for (int i = 0; i < NREAD; ++i) read_op(f0, smem, 0, i);
+
+  // One K-slice.  Each half is 16 steps of {memory op(s), one MFMA}, fenced so
+  // that the compiler keeps the interleaving: the MFMA pipe stays fed while the
+  // reads for the next half-slice and the loads for a later stage go out behind
+  // it.  The last slice runs the same body: its reads of the next stage and its
+  // (clamped) loads are in bounds and simply unused.
+  auto slice = [&](int kt, auto R) {
+    const int st = kt & (NST - 1);
+    const char* stage = smem + st * STAGEB;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < NREAD) read_op(f1, stage, 1, i);
+      mfma_op(f0, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    term_op(f0, 0, R);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice kt+1 has landed once at most NST-2 later slices are in flight
+    wait_vm<(NST - 2) * 2 * LPO>();
+    wait_lgkm0();  // this wave's reads of `stage` are done before anyone refills it
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const int ks = kt + NST < nk ? kt + NST : nk - 1;
+    const char* next = smem + ((kt + 1) & (NST - 1)) * STAGEB;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i < LPO) sp.issue_one(ks, ring + st * STAGEB, i);
+      else if (i < 2 * LPO) sq.issue_one(ks, ring + st * STAGEB + OPB, i - LPO);
+      if (i < NREAD) read_op(f0, next, 0, i);
+      mfma_op(f1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    term_op(f1, 1, R);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using NoTerm = std::integral_constant<int, -1>;
+  if constexpr (MODE == GM_GRAM) {
+    for (int kt = 0; kt < nk; ++kt) slice(kt, NoTerm{});
+  } else {
+    // slices rel0 .. rel0+3 carry the s-multiple term for blocks 0..3 (rel0 + 3 < nk)
+    const int rel0 = __builtin_amdgcn_readfirstlane(8 * tr.ti + 4 * (MODE == GM_PROD ? wn : wm));
+    for (int kt = 0; kt < rel0; ++kt) slice(kt, NoTerm{});
+    slice(rel0 + 0, std::integral_constant<int, 0>{});
+    slice(rel0 + 1, std::integral_constant<int, 1>{});
+    slice(rel0 + 2, std::integral_constant<int, 2>{});
+    slice(rel0 + 3, std::integral_constant<int, 3>{});
+    for (int kt = rel0 + 4; kt < nk; ++kt) slice(kt, NoTerm{});
+  }
+  wait_vm<0>();  // no load may still target LDS: the ring is reused for the store
+  __syncthreads();
+  store_tile_lds<MODE>(acc, tr, g, smem, wave, lane);
+}
+
+hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, const GemmArgs& g) {
+  if (nblocks <= 0) return hipSuccess;
+  switch (mode) {
+    case GM_GRAM:
+      hipLaunchKernelGGL(k_gemm_bf16<GM_GRAM>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, g);
+      break;
+    case GM_POLY:
+      hipLaunchKernelGGL(k_gemm_bf16<GM_POLY>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, g);
+      break;
+    default:
+      hipLaunchKernelGGL(k_gemm_bf16<GM_PROD>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, g);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace muon

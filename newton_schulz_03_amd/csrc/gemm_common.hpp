@@ -1,0 +1,202 @@
+// Shared pieces of the matrix-core kernels: tile decode and epilogues.
+//
+// Every kernel computes one 256x256 tile D[p][q] = sum_k P[p][k] Q[q][k] with
+// 4 wavefronts in a 2x2 grid (128x128 each) of v_mfma 32x32 blocks.  Lane
+// (lr = lane % 32, lh = lane / 32) of wave (wm, wn) holds, in acc[mi][ni][4g+e],
+//   D[p0 + e][q]  with  p0 = wm*128 + mi*32 + 8g + 4lh,  q = wn*128 + ni*32 + lr.
+//
+//   GRAM  P = Q = rows of X          D = (X X^T) tile (ti, tj), ti <= tj
+//   POLY  P = Q = rows of A          D = (A A) tile (ti, tj), ti <= tj
+//   PROD  P = columns tj of X, Q = rows ti of B (or A):  D[p][q] = (B X)[ti*256+q][tj*256+p]
+#pragma once
+
+#include "device_common.hpp"
+
+namespace muon {
+
+enum GemmMode : int { GM_GRAM = 0, GM_POLY = 1, GM_PROD = 2 };
+
+// What each kernel accumulates and stores (s = init_scale):
+//   GRAM  acc = X X^T,            A  = out_scale * acc   (out_scale = b when c = 0, else 1)
+//   POLY  acc = A A + s A,        B  = c * acc = b A + c A A   (s = b/c)
+//   PROD  acc = Q X + s X,        X' = acc                     (s = a)
+// The s-multiple of the source tile is added inside the K loop by the bf16
+// kernel (matrix cores, see gemm_bf16.hip) and at store time by the fp32 one.
+struct GemmArgs {
+  int32_t cur;        // X buffer holding the current iterate
+  float init_scale;   // POLY: b/c;  PROD: a
+  float out_scale;    // GRAM: 1 or b;  POLY: c;  PROD: 1
+  int32_t use_poly;   // PROD: Q = B (1) or A (0)
+};
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
+    v[0] = __uint_as_float(w[0] << 16);
+    v[1] = __uint_as_float(w[0] & 0xffff0000u);
+    v[2] = __uint_as_float(w[1] << 16);
+    v[3] = __uint_as_float(w[1] & 0xffff0000u);
+  } else {
+    const u32x4_t w = ld16(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(w[e]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    u32x2_t w;
+    w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[0])) |
+           (static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[1])) << 16);
+    w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[2])) |
+           (static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[3])) << 16);
+    *reinterpret_cast<u32x2_t*>(p) = w;
+  } else {
+    u32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = __float_as_uint(v[e]);
+    st16(p, w);
+  }
+}
+
+// Upper-triangle tile (ti <= tj) number t of a T x T tile grid, row by row.
+__device__ __forceinline__ void sym_tile(int32_t t, int32_t T, int32_t& ti, int32_t& tj) {
+  int32_t i = 0;
+  while (t >= T - i) {
+    t -= T - i;
+    ++i;
+  }
+  ti = i;
+  tj = i + t;
+}
+
+struct TileRef {
+  MatDesc d;  // a register copy: the epilogue's stores cannot alias it
+  int32_t ti, tj;
+};
+
+// Block -> (matrix, tile) for the symmetric phases (GRAM, POLY) or the product.
+template <int MODE>
+__device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c) {
+  const int32_t b = xcd_remap(static_cast<int32_t>(blockIdx.x), static_cast<int32_t>(gridDim.x));
+  const int32_t* pre = c.prefix + (MODE == GM_PROD ? PH_PROD : PH_SYM) * (c.batch + 1);
+  const int j = find_matrix(pre, c.batch, b);
+  TileRef r;
+  r.d = c.desc[j];
+  const int32_t t = b - pre[j];
+  const int32_t ts = r.d.s_pad / kTile;
+  if constexpr (MODE == GM_PROD) {
+    r.ti = t % ts;  // tile row along the short side, fastest: neighbours share X columns
+    r.tj = t / ts;
+  } else {
+    sym_tile(t, ts, r.ti, r.tj);
+  }
+  return r;
+}
+
+// Per-lane coordinates of the accumulator layout described above.
+struct LanePos {
+  int64_t row0, col0;  // PROD: output row (ti*256 + q0) and column (tj*256 + p0) of acc[0][0][0]
+  int64_t rq0, cp0;    // GRAM/POLY: the mirror position (row tj*256 + q0, column ti*256 + p0)
+};
+
+__device__ __forceinline__ LanePos lane_pos(const TileRef& tr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  LanePos lp;
+  lp.row0 = static_cast<int64_t>(tr.ti) * kTile + wn * 128 + lr;
+  lp.col0 = static_cast<int64_t>(tr.tj) * kTile + wm * 128 + 4 * lh;
+  lp.rq0 = static_cast<int64_t>(tr.tj) * kTile + wn * 128 + lr;
+  lp.cp0 = static_cast<int64_t>(tr.ti) * kTile + wm * 128 + 4 * lh;
+  return lp;
+}
+
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+}
+
+// Stores the finished tile.  With ADD_TERM the accumulated sum does not yet
+// hold the init_scale multiple of the source tile (X for the product, A for
+// the polynomial); it is read and added here, one row of blocks at a time.
+template <typename T, int MODE, bool ADD_TERM>
+__device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const TileRef& tr,
+                                           const GemmArgs& g) {
+  const LanePos lp = lane_pos(tr);
+  const int64_t s_pad = tr.d.s_pad, l_pad = tr.d.l_pad;
+  if constexpr (MODE == GM_PROD) {
+    const T* __restrict__ xin = static_cast<const T*>(tr.d.x[g.cur]);
+    T* __restrict__ xout = static_cast<T*>(tr.d.x[g.cur ^ 1]);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      float x[4][4][4];
+      if constexpr (ADD_TERM) {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+            load4<T>(xin + (lp.row0 + ni * 32) * l_pad + lp.col0 + mi * 32 + 8 * gg, x[ni][gg]);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = acc[mi][ni][4 * gg + e];
+            if constexpr (ADD_TERM) v[e] += g.init_scale * x[ni][gg][e];
+          }
+          store4<T>(xout + (lp.row0 + ni * 32) * l_pad + lp.col0 + mi * 32 + 8 * gg, v);
+        }
+    }
+  } else {
+    // D[p][q] = S[ti*256 + p][tj*256 + q] of the symmetric result S; the lane's
+    // four consecutive p are contiguous in row (tj*256 + q) of S (the mirror).
+    T* __restrict__ out = static_cast<T*>(MODE == GM_GRAM ? tr.d.gram : tr.d.poly);
+    const T* __restrict__ gram = static_cast<const T*>(tr.d.gram);
+    const bool offdiag = tr.ti != tr.tj;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      float av[4][4][4];
+      if constexpr (ADD_TERM && MODE == GM_POLY) {
+        // A[ti*256+p][tj*256+q] = A[tj*256+q][ti*256+p]: A is stored symmetric
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+            load4<T>(gram + (lp.rq0 + ni * 32) * s_pad + lp.cp0 + mi * 32 + 8 * gg, av[ni][gg]);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float t = acc[mi][ni][4 * gg + e];
+            if constexpr (ADD_TERM && MODE == GM_POLY) t += g.init_scale * av[ni][gg][e];
+            v[e] = g.out_scale * t;
+          }
+          const int64_t rq = lp.rq0 + ni * 32, cp = lp.cp0 + mi * 32 + 8 * gg;
+          store4<T>(out + rq * s_pad + cp, v);
+          if (offdiag) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[(cp + e) * s_pad + rq] = Elt<T>::from_f32(v[e]);
+          }
+        }
+    }
+  }
+}
+
+// Launches of the bf16 pipelined kernels (gemm_bf16.hip).
+hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, const GemmArgs& g);
+
+}  // namespace muon

@@ -297,7 +297,8 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   for (int k = 0; k < ns.steps; ++k) {
     {
       TimedLaunch t(MUON_K_GRAM, stream);
-      if ((e = launch_gram(c, pl.totals[PH_SYM], pl.bf16, cur)) != hipSuccess)
+      if ((e = launch_gram(c, pl.totals[PH_SYM], pl.bf16, cur, use_poly ? 1.f : ns.b)) !=
+          hipSuccess)
         return hip_fail(e, "launch Gram");
       t.done();
     }
@@ -309,8 +310,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
     }
     {
       TimedLaunch t(MUON_K_PROD, stream);
-      if ((e = launch_prod(c, pl.totals[PH_PROD], pl.bf16, cur, ns.a, use_poly ? 1.f : ns.b,
-                           use_poly)) != hipSuccess)
+      if ((e = launch_prod(c, pl.totals[PH_PROD], pl.bf16, cur, ns.a, use_poly)) != hipSuccess)
         return hip_fail(e, "launch product");
       t.done();
     }

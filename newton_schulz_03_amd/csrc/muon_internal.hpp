@@ -62,10 +62,13 @@ struct ElemParams {
 hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 hipError_t launch_normalize(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 hipError_t launch_finish(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
-hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur);
+// A = out_scale * X X^T  (out_scale = b when the polynomial has no A^2 term, else 1)
+hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
+                       float out_scale);
+// B = b A + c A A  (c != 0)
 hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc);
-// X[next] = a * X[cur] + alpha * (Q X[cur]) with Q = B (use_poly) or A.
+// X[next] = a X[cur] + Q X[cur] with Q = B (use_poly) or the already scaled A.
 hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur, float a,
-                       float alpha, bool use_poly);
+                       bool use_poly);
 
 }  // namespace muon
