@@ -112,6 +112,19 @@ __device__ __forceinline__ int find_matrix(const int32_t* prefix, int batch, int
   return lo;
 }
 
+// Slab layout of every workspace matrix (the iterate X, A and B): a padded
+// matrix with `ncols` columns is cut into slabs of kSlabRows x kSlabCols
+// elements, each stored contiguously and row-major; the slabs of one band of
+// kSlabRows rows follow each other.  A K-slice of 32 columns of a 256-row
+// band is then one contiguous run of memory, which is what the matrix-core
+// kernels stream into LDS.
+constexpr int kSlabRows = kTile;  // 256
+constexpr int kSlabCols = 32;
+__device__ __forceinline__ int64_t slab_off(int64_t r, int64_t c, int64_t ncols) {
+  return ((r / kSlabRows) * (ncols / kSlabCols) + c / kSlabCols) * (kSlabRows * kSlabCols) +
+         (r % kSlabRows) * kSlabCols + (c % kSlabCols);
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs of the chip (block b runs on
 // XCD b % 8).  Renumber them so that each XCD receives one contiguous range of
 // logical blocks: neighbouring tiles, which share operands, then share an L2.

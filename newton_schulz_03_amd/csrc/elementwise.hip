@@ -173,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void k_normalize(LaunchCtx c, ElemParams 
 #pragma unroll
     for (int e = 0; e < 16; ++e) u[e] = tile[cc + e][rr];
   }
-  T* x0 = static_cast<T*>(d.x[0]) + (i0 + rr) * d.l_pad + j0 + cc;
+  // 16 consecutive columns starting at a multiple of 16 stay inside one slab row
+  T* x0 = static_cast<T*>(d.x[0]) + slab_off(i0 + rr, j0 + cc, d.l_pad);
 #pragma unroll
   for (int q = 0; q < 16 / V; ++q) st16(x0 + q * V, f32_to_vec<T>(u + q * V));
 }
@@ -197,12 +198,12 @@ __global__ __launch_bounds__(kThreads) void k_finish(LaunchCtx c, ElemParams p) 
   const T* X = static_cast<const T*>(d.x[p.cur]);
   float o[16];
   if (!d.tall) {
-    const T* src = X + (r0 + rr) * d.l_pad + c0 + cc;  // inside the padded buffer
+    const T* src = X + slab_off(r0 + rr, c0 + cc, d.l_pad);  // inside the padded buffer
 #pragma unroll
     for (int q = 0; q < 16 / V; ++q) vec_to_f32<T>(ld16(src + q * V), o + q * V);
   } else {
     // O[r][c] = X[c][r]: stage the wide tile (rows c0.., cols r0..) through LDS
-    const T* src = X + (c0 + rr) * d.l_pad + r0 + cc;
+    const T* src = X + slab_off(c0 + rr, r0 + cc, d.l_pad);
     float v[16];
 #pragma unroll
     for (int q = 0; q < 16 / V; ++q) vec_to_f32<T>(ld16(src + q * V), v + q * V);

@@ -44,11 +44,11 @@ template <typename T>
 struct KMajorTile {
   static constexpr int V = Elt<T>::kVec;
   u32x4_t r[8];
-  __device__ __forceinline__ void load(const T* rows, int64_t ld, int64_t k0) {
+  // rows [row0, row0 + 256) of a slab-layout matrix with ld columns, columns [k0, k0 + BK)
+  __device__ __forceinline__ void load(const T* m, int64_t row0, int64_t ld, int64_t k0) {
     const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
-    const T* p = rows + static_cast<int64_t>(r0) * ld + k0 + c * V;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) r[u] = ld16(p + static_cast<int64_t>(32 * u) * ld);
+    for (int u = 0; u < 8; ++u) r[u] = ld16(m + slab_off(row0 + r0 + 32 * u, k0 + c * V, ld));
   }
   __device__ __forceinline__ void store(char* lds) const {
     const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
@@ -67,14 +67,14 @@ struct MNMajorTile {
   static constexpr int KB = BK / V;              // blocks along K (8)
   static constexpr int PER = NB * KB / kThreads;  // blocks per thread: 1 (bf16), 2 (fp32)
   u32x4_t r[PER][V];
-  __device__ __forceinline__ void load(const T* cols, int64_t ld, int64_t k0) {
+  // rows [k0, k0 + BK) x columns [n0, n0 + 256) of a slab-layout matrix with ld columns
+  __device__ __forceinline__ void load(const T* m, int64_t n0, int64_t ld, int64_t k0) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int q = threadIdx.x + kThreads * p;
       const int nb = q % NB, kb = q / NB;
-      const T* src = cols + (k0 + kb * V) * ld + nb * V;
 #pragma unroll
-      for (int e = 0; e < V; ++e) r[p][e] = ld16(src + static_cast<int64_t>(e) * ld);
+      for (int e = 0; e < V; ++e) r[p][e] = ld16(m + slab_off(k0 + kb * V + e, n0 + nb * V, ld));
     }
   }
   __device__ __forceinline__ void store(char* lds) const {
@@ -129,23 +129,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
   const T* Xc = static_cast<const T*>(d.x[g.cur]);
 
   // Operand P (MFMA rows, index p) and Q (MFMA columns, index q): D[p][q] = sum_k P[p][k] Q[q][k].
-  const T* p_base;
-  const T* q_base;
-  int64_t p_ld, q_ld, K;
+  // p_at / q_at: first row (K-major) or first column (MN-major) of the tile's operand.
+  const T* p_m;
+  const T* q_m;
+  int64_t p_at, q_at, p_ld, q_ld, K;
   if constexpr (MODE == GM_GRAM) {
-    p_base = Xc + ti * kTile * l_pad;  p_ld = l_pad;
-    q_base = Xc + tj * kTile * l_pad;  q_ld = l_pad;
+    p_m = Xc;  p_at = ti * kTile;  p_ld = l_pad;
+    q_m = Xc;  q_at = tj * kTile;  q_ld = l_pad;
     K = l_pad;
   } else if constexpr (MODE == GM_POLY) {
     const T* A = static_cast<const T*>(d.gram);
-    p_base = A + ti * kTile * s_pad;  p_ld = s_pad;
-    q_base = A + tj * kTile * s_pad;  q_ld = s_pad;
+    p_m = A;  p_at = ti * kTile;  p_ld = s_pad;
+    q_m = A;  q_at = tj * kTile;  q_ld = s_pad;
     K = s_pad;
   } else {
     // P = columns tj of X (transposed on the way into LDS), Q = rows ti of B (or A)
-    const T* Q = static_cast<const T*>(g.use_poly ? d.poly : d.gram);
-    p_base = Xc + tj * kTile;  p_ld = l_pad;
-    q_base = Q + ti * kTile * s_pad;  q_ld = s_pad;
+    p_m = Xc;  p_at = tj * kTile;  p_ld = l_pad;
+    q_m = static_cast<const T*>(g.use_poly ? d.poly : d.gram);  q_at = ti * kTile;  q_ld = s_pad;
     K = s_pad;
   }
 
@@ -161,8 +161,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
   zero_acc(acc);
 
   const int nk = static_cast<int>(K / BK);
-  pt.load(p_base, p_ld, 0);
-  qt.load(q_base, q_ld, 0);
+  pt.load(p_m, p_at, p_ld, 0);
+  qt.load(q_m, q_at, q_ld, 0);
   pt.store(smem);
   qt.store(smem + kOpBytes);
   __syncthreads();
@@ -171,8 +171,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
     char* stage = smem + (kt & 1) * kStageBytes;
     const bool more = kt + 1 < nk;
     if (more) {
-      pt.load(p_base, p_ld, static_cast<int64_t>(kt + 1) * BK);
-      qt.load(q_base, q_ld, static_cast<int64_t>(kt + 1) * BK);
+      pt.load(p_m, p_at, p_ld, static_cast<int64_t>(kt + 1) * BK);
+      qt.load(q_m, q_at, q_ld, static_cast<int64_t>(kt + 1) * BK);
     }
     const char* P = stage;
     const char* Q = stage + kOpBytes;

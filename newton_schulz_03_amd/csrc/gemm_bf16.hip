@@ -7,15 +7,17 @@
 //    lane's 16 bytes straight into LDS (lane i at base + 16 i).  The LDS layout
 //    is therefore chosen by permuting which global chunk each lane fetches.
 //  * A ring of 4 LDS stages of 32 K-values (P and Q tiles of 256 x 32 bf16,
-//    32 KiB per stage, 128 KiB in all): k-slice j is requested three slices
-//    before it is consumed, and one barrier per slice suffices.
-//  * K-major operands (rows of X, A or B) are kept as 64-byte rows, their four
-//    16-byte chunks XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3 so that the
-//    fragment reads (8 consecutive rows per 128 bytes of banks) do not collide.
-//  * The MN-major operand of the product (X read along its columns) stays in
-//    its natural layout, [k][n] with 512-byte rows, chunks swizzled by
-//    2 (k & 3); fragments are assembled with ds_read_b64_tr_b16, whose 16-lane
-//    groups read a 4 x 16 block and hand each lane one column.
+//    32 KiB per stage, 128 KiB in all): k-slice j is requested while slice
+//    j-3 is consumed, and one barrier per slice suffices.
+//  * Workspace matrices are stored in 256 x 32 slabs, so each slice of a
+//    K-major operand (rows of X, A or B) is one contiguous 16 KiB slab and each
+//    load instruction reads 1 KiB of consecutive bytes.  In LDS the slab keeps
+//    its 64-byte rows, their four 16-byte chunks XOR-swizzled by
+//    ((row >> 1) ^ (row >> 3)) & 3 so that the fragment reads do not collide.
+//  * The MN-major operand of the product (X read along its columns) arrives as
+//    8 pieces of 32 rows x 64 bytes (one per slab), chunks swizzled by
+//    2 ((row >> 1) & 1); fragments are assembled with ds_read_b64_tr_b16, whose
+//    16-lane groups read a 4 x 16 block and hand each lane one column.
 //  * Fragments are software-pipelined across the slice boundary: the reads of
 //    the next slice's first half overlap the MFMAs of this slice's second half.
 #include "gemm_common.hpp"
@@ -32,6 +34,7 @@ constexpr int NST = 4;                      // stages in the ring
 constexpr int LDSB = NST * STAGEB;          // 128 KiB
 constexpr int LPO = OPB / (kThreads * 16);  // 16-byte loads per thread, operand and stage (4)
 constexpr int MNROW = kTile * 2;            // bytes of one MN-major LDS row (256 columns)
+static_assert(LDSB >= kTile * MNROW, "the tile store stages a whole 256 x 256 bf16 tile in the ring");
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -61,28 +64,32 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, int32_t voff, i32x4
                : "memory", "m0");
 }
 
-// One operand's stream of 256 x 32 tiles into the LDS ring.
+// One operand's stream of 256 x 32 tiles into the LDS ring.  In the slab layout
+// (slab_off in device_common.hpp) a K-major tile is one contiguous 16 KiB slab;
+// the product's MN-major tile (32 rows of X x 256 columns) is 8 contiguous
+// 2 KiB pieces, one per slab.
 struct Stream {
-  const char* base;     // byte address of the operand tile at k-slice 0 (uniform)
-  int64_t step;         // bytes the base advances per k-slice
-  int64_t extent;       // bytes addressable from base at k-slice 0
-  int32_t voff[LPO];    // per-lane byte offsets, one per load instruction
-  int32_t lds;          // LDS byte offset of this wave's first 1 KiB block, within the operand
+  const char* base;      // byte address at k-slice 0 (uniform)
+  int64_t band_stride;   // MN-major: bytes between bands of 256 rows
+  int32_t mn;            // 1: MN-major, 0: K-major
+  int32_t voff[LPO];     // per-lane byte offsets, one per load instruction
+  int32_t lds;           // LDS byte offset of this wave's first 1 KiB block, within the operand
 
   // Buffer resource for k-slice ks: base, stride 0, num_records (bytes), raw dword access.
   __device__ __forceinline__ i32x4_t rsrc(int ks) const {
-    const uint64_t b = reinterpret_cast<uint64_t>(base) + static_cast<uint64_t>(ks) * step;
-    const int64_t left = extent - static_cast<int64_t>(ks) * step;
+    const uint64_t b = reinterpret_cast<uint64_t>(base) +
+                       (mn ? static_cast<uint64_t>(ks >> 3) * band_stride +
+                                 static_cast<uint64_t>(ks & 7) * (32 * KROW)
+                           : static_cast<uint64_t>(ks) * OPB);
     i32x4_t r;
     r[0] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(b & 0xffffffffu));
     r[1] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((b >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane(
-        static_cast<int32_t>(left > 0x7fffffffLL ? 0x7fffffffLL : (left < 0 ? 0 : left)));
+    r[2] = mn ? 7 * OPB + 32 * KROW : OPB;  // exactly the bytes this slice reads
     r[3] = 0x00020000;
     return r;
   }
-  __device__ __forceinline__ void issue_one(int ks, uint32_t stage_op_lds, int u) const {
-    lds_dma16(__builtin_amdgcn_readfirstlane(stage_op_lds + lds + u * 1024), voff[u], rsrc(ks));
+  __device__ __forceinline__ void issue_one(const i32x4_t& r, uint32_t stage_op_lds, int u) const {
+    lds_dma16(__builtin_amdgcn_readfirstlane(stage_op_lds + lds + u * 1024), voff[u], r);
   }
   __device__ __forceinline__ void issue(int ks, uint32_t stage_op_lds) const {
     const i32x4_t r = rsrc(ks);
@@ -92,35 +99,40 @@ struct Stream {
   }
 };
 
-// Rows [row0, row0+256) of a row-major matrix (leading dimension ld), K along the row.
-__device__ __forceinline__ Stream kmajor_stream(const uint16_t* m, int64_t row0, int64_t ld,
-                                                int64_t K, int wave, int lane) {
+// Rows [256 band, 256 band + 256) of a slab-layout matrix with `ncols` columns.
+// LDS: 256 rows of 64 bytes, chunk c of row r kept at c ^ kkey(r).
+__device__ __forceinline__ Stream kmajor_stream(const uint16_t* m, int64_t band, int64_t ncols,
+                                                int wave, int lane) {
   Stream s;
-  s.base = reinterpret_cast<const char*>(m + row0 * ld);
-  s.step = KROW;
-  s.extent = (255 * ld + K) * 2;
+  s.base = reinterpret_cast<const char*>(m + band * (ncols / kSlabCols) * (kSlabRows * kSlabCols));
+  s.band_stride = 0;
+  s.mn = 0;
 #pragma unroll
   for (int u = 0; u < LPO; ++u) {
     const int row = 16 * (LPO * wave + u) + (lane >> 2);
     const int c = (lane & 3) ^ kkey(row);
-    s.voff[u] = static_cast<int32_t>(row * ld * 2 + c * 16);
+    s.voff[u] = row * KROW + c * 16;
   }
   s.lds = LPO * wave * 1024;
   return s;
 }
 
-// Columns [n0, n0+256) of a row-major matrix with K rows, K along the column.
-__device__ __forceinline__ Stream mnmajor_stream(const uint16_t* m, int64_t n0, int64_t ld,
-                                                 int64_t K, int wave, int lane) {
+// Columns [256 tj, 256 tj + 256) of a slab-layout matrix (all its rows, 32 per
+// k-slice).  LDS: 8 pieces (one per slab) of 32 rows x 64 bytes, chunk c of row
+// r kept at c ^ (2 ((r >> 1) & 1)).
+__device__ __forceinline__ Stream mnmajor_stream(const uint16_t* m, int64_t tj, int64_t ncols,
+                                                 int wave, int lane) {
   Stream s;
-  s.base = reinterpret_cast<const char*>(m + n0);
-  s.step = static_cast<int64_t>(BK) * ld * 2;
-  s.extent = ((K - 1) * ld + kTile) * 2;
+  const int64_t slabs_per_band = ncols / kSlabCols;
+  s.base = reinterpret_cast<const char*>(m + 8 * tj * (kSlabRows * kSlabCols));
+  s.band_stride = slabs_per_band * OPB;
+  s.mn = 1;
 #pragma unroll
   for (int u = 0; u < LPO; ++u) {
-    const int k = 2 * (LPO * wave + u) + (lane >> 5);
-    const int c = (lane & 31) ^ (2 * (k & 3));
-    s.voff[u] = static_cast<int32_t>(k * ld * 2 + c * 16);
+    const int blk = LPO * wave + u;  // 1 KiB block: slab piece blk / 2, rows 16 (blk % 2) ..
+    const int row = 16 * (blk & 1) + (lane >> 2);
+    const int c = (lane & 3) ^ (2 * ((row >> 1) & 1));
+    s.voff[u] = (blk >> 1) * OPB + row * KROW + c * 16;
   }
   s.lds = LPO * wave * 1024;
   return s;
@@ -199,7 +211,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
     for (int u = 0; u < 32; ++u) {
       const int q = (t >> 5) + 8 * u;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4));
-      st16(dst + (r0 + q) * ld + c0 + 8 * c, v);
+      st16(dst + slab_off(r0 + q, c0 + 8 * c, ld), v);
     }
   }
   if constexpr (MODE != GM_PROD) {
@@ -228,7 +240,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
           v[2 * h] = xu[0];
           v[2 * h + 1] = xu[1];
         }
-        st16(dst + (r0 + 16 * pb + j) * ld + c0 + 8 * cq, v);
+        st16(dst + slab_off(r0 + 16 * pb + j, c0 + 8 * cq, ld), v);
       }
     }
   }
@@ -254,18 +266,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   int64_t K;
   if constexpr (MODE == GM_GRAM) {
     K = l_pad;
-    sp = kmajor_stream(Xc, static_cast<int64_t>(tr.ti) * kTile, l_pad, K, wave, lane);
-    sq = kmajor_stream(Xc, static_cast<int64_t>(tr.tj) * kTile, l_pad, K, wave, lane);
+    sp = kmajor_stream(Xc, tr.ti, l_pad, wave, lane);
+    sq = kmajor_stream(Xc, tr.tj, l_pad, wave, lane);
   } else if constexpr (MODE == GM_POLY) {
     K = s_pad;
     const uint16_t* A = static_cast<const uint16_t*>(d.gram);
-    sp = kmajor_stream(A, static_cast<int64_t>(tr.ti) * kTile, s_pad, K, wave, lane);
-    sq = kmajor_stream(A, static_cast<int64_t>(tr.tj) * kTile, s_pad, K, wave, lane);
+    sp = kmajor_stream(A, tr.ti, s_pad, wave, lane);
+    sq = kmajor_stream(A, tr.tj, s_pad, wave, lane);
   } else {
     K = s_pad;
     const uint16_t* Q = static_cast<const uint16_t*>(g.use_poly ? d.poly : d.gram);
-    sp = mnmajor_stream(Xc, static_cast<int64_t>(tr.tj) * kTile, l_pad, K, wave, lane);
-    sq = kmajor_stream(Q, static_cast<int64_t>(tr.ti) * kTile, s_pad, K, wave, lane);
+    sp = mnmajor_stream(Xc, tr.tj, l_pad, wave, lane);
+    sq = kmajor_stream(Q, tr.ti, s_pad, wave, lane);
   }
   const int nk = static_cast<int>(K / BK);
 
@@ -278,14 +290,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
     qoff[sub] = OPB + (wn * 128 + lr) * KROW + sw;
     poff[sub] = (wm * 128 + lr) * KROW + sw;
   }
-  //  MN-major (product): 16-lane group gq, source row r, column quad qq
-  int32_t moff[4];
+  //  MN-major (product): 16-lane group gq, source row r, column quad qq.  The
+  //  lane points at row 8 (gq >> 1) + r (+ 16 sub + 4 h) of slab piece 4 wm + mi,
+  //  columns 16 (gq & 1) + 4 qq .. + 3.
+  int32_t moff0;
   {
     const int gq = lane >> 4, r = (lane >> 2) & 3, qq = lane & 3;
-    const int t0 = (8 * (gq >> 1) + r) * MNROW + 8 * (qq & 1);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      moff[mi] = t0 + ((((16 * wm + 4 * mi + 2 * (gq & 1) + (qq >> 1))) ^ (2 * r)) << 4);
+    const int c = 2 * (gq & 1) + (qq >> 1);
+    moff0 = 4 * wm * (32 * KROW) + (8 * (gq >> 1) + r) * KROW + ((c ^ (2 * ((r >> 1) & 1))) << 4) +
+            8 * (qq & 1);
   }
 
   // Fragment reads, numbered in the order the MFMAs below consume them:
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   auto read_op = [&](Frags& f, const char* stage, int sub, int i) {
     if constexpr (MODE == GM_PROD) {
       if (i < 2) {
-        const char* base = stage + moff[0] + 16 * sub * MNROW + 4 * i * MNROW;
+        const char* base = stage + moff0 + (16 * sub + 4 * i) * KROW;
         const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(base));
         const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
         f.p[0][2 * i] = u[0];
@@ -303,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
         f.q[i - 2] = lds16(stage + qoff[sub] + (i - 2) * 32 * KROW);
       } else {
         const int mi = 1 + (i - 6) / 2, h = (i - 6) % 2;
-        const char* base = stage + moff[mi] + 16 * sub * MNROW + 4 * h * MNROW;
+        const char* base = stage + moff0 + mi * (32 * KROW) + (16 * sub + 4 * h) * KROW;
         const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(base));
         const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
         f.p[mi][2 * h] = u[0];
@@ -368,16 +381,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   // LDS byte address of the ring (the low 32 bits of an LDS pointer are its offset).
   const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)smem));
 
-  // Prologue: request slices 0..NST-1, wait for slice 0.  Slice indices past the
+  // Prologue: request slices 0..NST-2, wait for slice 0.  Slice indices past the
   // end are clamped to the last slice: the extra loads refill a stage nobody
   // reads again and keep the count of loads in flight the same every iteration.
 #pragma unroll
-  for (int s = 0; s < NST; ++s) {
+  for (int s = 0; s < NST - 1; ++s) {
     const int ks = s < nk ? s : nk - 1;
     sp.issue(ks, ring + s * STAGEB);
     sq.issue(ks, ring + s * STAGEB + OPB);
   }
-  wait_vm<(NST - 1) * 2 * LPO>();
+  wait_vm<(NST - 2) * 2 * LPO>();
   __syncthreads();
 
   Frags f0, f1;
@@ -389,28 +402,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   // reads for the next half-slice and the loads for a later stage go out behind
   // it.  The last slice runs the same body: its reads of the next stage and its
   // (clamped) loads are in bounds and simply unused.
+  // Slice kt: stage kt is read; stage kt+NST-1 (the one slice kt-1 used) is
+  // refilled with slice kt+NST-1, its P loads in the first half and its Q loads
+  // in the second, so that the address path sees one load every few MFMAs.
   auto slice = [&](int kt, auto R) {
     const int st = kt & (NST - 1);
     const char* stage = smem + st * STAGEB;
+    const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
+    const uint32_t fill = ring + ((kt + NST - 1) & (NST - 1)) * STAGEB;
+    const i32x4_t rp = sp.rsrc(ks);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      if ((i & 3) == 0) sp.issue_one(rp, fill, i >> 2);
       if (i < NREAD) read_op(f1, stage, 1, i);
       mfma_op(f0, i);
       __builtin_amdgcn_sched_barrier(0);
     }
     term_op(f0, 0, R);
     __builtin_amdgcn_sched_barrier(0);
-    // slice kt+1 has landed once at most NST-2 later slices are in flight
-    wait_vm<(NST - 2) * 2 * LPO>();
-    wait_lgkm0();  // this wave's reads of `stage` are done before anyone refills it
+    // slice kt+1 has landed once only slice kt+2 and the P half of kt+NST-1 remain
+    wait_vm<(NST - 3) * 2 * LPO + LPO>();
+    wait_lgkm0();  // this wave's reads of `stage` are done before the next refill
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    const int ks = kt + NST < nk ? kt + NST : nk - 1;
+    const i32x4_t rq = sq.rsrc(ks);
     const char* next = smem + ((kt + 1) & (NST - 1)) * STAGEB;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i < LPO) sp.issue_one(ks, ring + st * STAGEB, i);
-      else if (i < 2 * LPO) sq.issue_one(ks, ring + st * STAGEB + OPB, i - LPO);
+      if ((i & 3) == 0) sq.issue_one(rq, fill + OPB, i >> 2);
       if (i < NREAD) read_op(f0, next, 0, i);
       mfma_op(f1, i);
       __builtin_amdgcn_sched_barrier(0);

@@ -142,7 +142,7 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
           for (int gg = 0; gg < 4; ++gg)
-            load4<T>(xin + (lp.row0 + ni * 32) * l_pad + lp.col0 + mi * 32 + 8 * gg, x[ni][gg]);
+            load4<T>(xin + slab_off(lp.row0 + ni * 32, lp.col0 + mi * 32 + 8 * gg, l_pad), x[ni][gg]);
       }
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
@@ -154,7 +154,7 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
             v[e] = acc[mi][ni][4 * gg + e];
             if constexpr (ADD_TERM) v[e] += g.init_scale * x[ni][gg][e];
           }
-          store4<T>(xout + (lp.row0 + ni * 32) * l_pad + lp.col0 + mi * 32 + 8 * gg, v);
+          store4<T>(xout + slab_off(lp.row0 + ni * 32, lp.col0 + mi * 32 + 8 * gg, l_pad), v);
         }
     }
   } else {
@@ -172,7 +172,7 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
           for (int gg = 0; gg < 4; ++gg)
-            load4<T>(gram + (lp.rq0 + ni * 32) * s_pad + lp.cp0 + mi * 32 + 8 * gg, av[ni][gg]);
+            load4<T>(gram + slab_off(lp.rq0 + ni * 32, lp.cp0 + mi * 32 + 8 * gg, s_pad), av[ni][gg]);
       }
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
@@ -186,10 +186,10 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
             v[e] = g.out_scale * t;
           }
           const int64_t rq = lp.rq0 + ni * 32, cp = lp.cp0 + mi * 32 + 8 * gg;
-          store4<T>(out + rq * s_pad + cp, v);
+          store4<T>(out + slab_off(rq, cp, s_pad), v);
           if (offdiag) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[(cp + e) * s_pad + rq] = Elt<T>::from_f32(v[e]);
+            for (int e = 0; e < 4; ++e) out[slab_off(cp + e, rq, s_pad)] = Elt<T>::from_f32(v[e]);
           }
         }
     }

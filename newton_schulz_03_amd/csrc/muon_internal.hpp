@@ -8,7 +8,8 @@
 // with more rows than columns is transposed on the way in and back on the way
 // out.  s_pad and l_pad round the short and long sides up to the GEMM tile
 // (256); the padding holds zeros, which the iteration keeps at zero, so the
-// product kernels need no bounds checks.
+// product kernels need no bounds checks.  X, A and B are stored in slabs of
+// 256 x 32 elements (see slab_off in device_common.hpp).
 #pragma once
 
 #include <hip/hip_runtime.h>
