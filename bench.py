@@ -22,7 +22,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+from newton_schulz_03_amd import rocprof_summary  # noqa: E402  (plain Python, loads no library)
+
 METRIC = "expert matrices orthogonalized/sec + % bf16 MFMA peak (6144×2048, 5 NS steps)"
+# HBM traffic of the product kernel per launch, from hardware counters (FETCH_SIZE and
+# WRITE_SIZE, scaled by a copy of known size); used while the kernel sources are unchanged
+TRAFFIC_WORKLOAD = "c2_96x2048x6144"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_prod_c2_96x2048x6144.md")
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # dense matrix-core peaks at 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
@@ -65,8 +71,12 @@ def make_inputs(wl, device, threads=16):
     return out
 
 
-def cpu_baseline(wl, sample: int):
-    """The float64 oracle on `sample` matrices of the same workload, timed on the host."""
+def cpu_baseline(wl, seconds: float, max_sample: int):
+    """The float64 oracle on the first matrices of the same workload, timed on the host.
+
+    Matrices are run one after another until `seconds` of oracle time have
+    passed (at least one, at most `max_sample`); input generation is not timed.
+    """
     import numpy as np
 
     import oracle
@@ -78,21 +88,23 @@ def cpu_baseline(wl, sample: int):
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
     except Exception:  # pragma: no cover - threadpoolctl missing
         cores = os.cpu_count() or 1
-    host = []
-    for j in range(sample):
-        raw = workloads.matrix_inputs(wl, j)
-        host.append({k: workloads.as_float64(workloads.cast(v, wl.dtype)) for k, v in raw.items()})
-    t0 = time.perf_counter()
-    for h in host:
+    dt = 0.0
+    sample = 0
+    while sample < min(max_sample, wl.batch) and (sample == 0 or dt < seconds):
+        raw = workloads.matrix_inputs(wl, sample)
+        h = {k: workloads.as_float64(workloads.cast(v, wl.dtype)) for k, v in raw.items()}
+        t0 = time.perf_counter()
         if wl.call == "step":
             oracle.muon_step(h["w"], h["g"], h["m"], lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov,
                              steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps)
         else:
             oracle.newton_schulz(h["x"], wl.steps, wl.coeffs, wl.eps)
-    dt = time.perf_counter() - t0
-    return {"value": sample / dt, "unit": "matrices/s", "cores": cores, "kind": "oracle",
-            "sample": f"{sample} of {wl.batch} matrices {list(wl.shapes[0])}, float64 numpy, "
-                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+        dt += time.perf_counter() - t0
+        sample += 1
+    shapes = sorted({tuple(s) for s in wl.shapes[:sample]})
+    return {"value": round(sample / dt, 4), "unit": "matrices/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {sample} of {wl.batch} matrices {shapes} of {wl.name}, full step "
+                      f"in float64 numpy, {dt:.1f} s of oracle time", "seconds": round(dt, 2)}
 
 
 def main(argv=None) -> int:
@@ -101,7 +113,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="c2_96x2048x6144")
-    ap.add_argument("--cpu-sample", type=int, default=2, help="matrices timed on the oracle")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time for the CPU baseline (whole matrices, at least one)")
+    ap.add_argument("--cpu-max-sample", type=int, default=64, help="most matrices timed on the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
@@ -109,9 +123,9 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
-              "multi-GPU path (matrices are independent; see the sharding notes in DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library orthogonalizes a ragged batch on a single "
+              "MI355X and has no multi-GPU path (matrices are independent, so each rank would run "
+              "its own share of whole matrices).", file=sys.stderr)
         return 2
 
     import torch
@@ -216,24 +230,27 @@ def main(argv=None) -> int:
                    "nesterov": wl.nesterov, "lr": wl.lr, "beta": wl.beta},
         "roofline": {"bound": "mfma", "kernel": "prod (X <- aX + BX)", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None},
+                     "traffic": rocprof_summary.read_traffic(TRAFFIC_SUMMARY, wl.name)
+                     if wl.name == TRAFFIC_WORKLOAD else None},
         "ns_effective_tflops": round(alg_total / (total_ms / args.steps * 1e-3) / 1e12, 1),
         "ns_mfma_frac_whole_step": round(alg_total / (total_ms / args.steps * 1e-3) / 1e12 / peak, 4),
         "ns_kernels_ms_per_step": round(ns_ms, 3),
         "kernels": per_kernel,
     }
     if args.copy_calibration_mb > 0:
+        # one plain copy of known size (reads n bytes, writes n bytes): hardware
+        # traffic counters of the same run are scaled by what they read for it
         n = args.copy_calibration_mb * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.full((n // 4,), 1.5, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize(dev)
-        dst.copy_(src)
+        torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize(dev)
         result["copy_calibration_bytes"] = n
         del src, dst
     if not args.no_cpu_baseline:
-        print(f"[bench] timing the oracle on {args.cpu_sample} matrices", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+        print(f"[bench] timing the oracle for about {args.cpu_seconds:.0f} s", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, args.cpu_max_sample)
     print(json.dumps(result), flush=True)
     return 0
 

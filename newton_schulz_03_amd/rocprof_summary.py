@@ -1,0 +1,175 @@
+"""Summaries of rocprofv3 output for the Muon kernels, as short markdown.
+
+Usage:
+    python -m newton_schulz_03_amd.rocprof_summary trace DIR --command "..."
+        DIR holds the CSV output of `rocprofv3 --kernel-trace --stats`:
+        a per-kernel table of calls and durations.
+    python -m newton_schulz_03_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
+            --copy-bytes N --workload NAME --command "..."
+        FETCH_DIR and WRITE_DIR hold the CSV output of two runs, one with
+        `--pmc FETCH_SIZE` and one with `--pmc WRITE_SIZE`.  In both runs the
+        program also ran one plain device copy of N bytes (read N, write N;
+        a float32 multiply by 2 into another buffer, torch's MulFunctor kernel).
+        Its counter readings give the scale from counter units to bytes.  Prints the
+        per-dispatch HBM traffic of every Muon kernel and a machine-readable
+        block for the product kernel, which the benchmark reads back as long
+        as the kernel sources are unchanged (same digest).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+# Sources that determine the matrix-core kernels' memory traffic.
+KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_common.hpp",
+                  "csrc/muon_internal.hpp", "csrc/muon_abi.hip")
+
+SHORT_NAMES = (("k_gemm_bf16<0>", "gram"), ("k_gemm_bf16<1>", "poly"), ("k_gemm_bf16<2>", "prod"),
+               ("k_gemm_staged", "gemm_fp32"), ("k_reduce", "reduce"), ("k_normalize", "normalize"),
+               ("k_finish", "finish"))
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(_PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def short_name(kernel: str) -> str:
+    k = kernel.replace("(int)", "").replace(" ", "")
+    for key, name in SHORT_NAMES:
+        if key.replace(" ", "") in k:
+            return name
+    if "MulFunctor" in kernel:
+        return "copy"
+    if "FillFunctor" in kernel:
+        return "fill"
+    return kernel[:48]
+
+
+def _one_csv(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def trace_table(d: str):
+    rows = list(csv.DictReader(open(_one_csv(d, "kernel_stats.csv"))))
+    out = []
+    for r in rows:
+        out.append((short_name(r["Name"]), r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e6,
+                    float(r["TotalDurationNs"]) / 1e6, float(r.get("Percentage", 0.0))))
+    out.sort(key=lambda x: -x[4])
+    return out
+
+
+def counter_per_dispatch(d: str, counter: str):
+    """kernel short name -> (dispatches, mean counter value per dispatch)."""
+    tot = collections.defaultdict(float)
+    disp = collections.defaultdict(set)
+    for r in csv.DictReader(open(_one_csv(d, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        k = short_name(r["Kernel_Name"])
+        tot[k] += float(r["Counter_Value"])
+        disp[k].add(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+    return {k: (len(disp[k]), tot[k] / max(1, len(disp[k]))) for k in tot}
+
+
+def cmd_trace(a):
+    rows = trace_table(a.dir)
+    print(f"# Kernel trace: {a.title}\n")
+    print(f"Command (from the repository root):\n\n```\n{a.command}\n```\n")
+    print("| kernel | calls | avg ms | total ms | % of GPU time |")
+    print("|---|---|---|---|---|")
+    for short, _, calls, avg, total, pct in rows:
+        print(f"| {short} | {calls} | {avg:.4f} | {total:.2f} | {pct:.1f} |")
+    print("\nFull kernel names:\n")
+    for short, name, *_ in rows:
+        print(f"- {short}: `{name[:160]}`")
+
+
+def cmd_traffic(a):
+    fetch = counter_per_dispatch(a.fetch_dir, "FETCH_SIZE")
+    write = counter_per_dispatch(a.write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("the calibration copy kernel is missing from the counter output")
+    ff = a.copy_bytes / (fetch["copy"][1] * 1024.0)
+    wf = a.copy_bytes / (write["copy"][1] * 1024.0)
+    print(f"# HBM traffic per dispatch: {a.workload}\n")
+    print("Commands (from the repository root, each a run of its own):\n")
+    print(f"```\n{a.command}\n```\n")
+    print(f"Calibration: one device copy of {a.copy_bytes} bytes reads "
+          f"{fetch['copy'][1]:.0f} KiB by FETCH_SIZE and writes {write['copy'][1]:.0f} KiB by "
+          f"WRITE_SIZE; scale factors {ff:.4f} (fetch) and {wf:.4f} (write).\n")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes (scaled) |")
+    print("|---|---|---|---|---|")
+    traffic = {}
+    for k in sorted(set(fetch) & set(write)):
+        b = fetch[k][1] * 1024.0 * ff + write[k][1] * 1024.0 * wf
+        traffic[k] = b
+        print(f"| {k} | {fetch[k][0]} | {fetch[k][1]:.0f} | {write[k][1]:.0f} | {b:.4g} |")
+    if "prod" in traffic:
+        print("\nProduct kernel, read back by the benchmark:\n")
+        print("```")
+        print("kernel: prod")
+        print(f"workload: {a.workload}")
+        print(f"source_sha256: {kernel_source_digest()}")
+        print(f"fetch_kib_per_dispatch: {fetch['prod'][1]:.1f}")
+        print(f"write_kib_per_dispatch: {write['prod'][1]:.1f}")
+        print(f"fetch_factor: {ff:.6f}")
+        print(f"write_factor: {wf:.6f}")
+        print(f"traffic_bytes_per_launch: {traffic['prod']:.0f}")
+        print("```")
+
+
+def read_traffic(path: str, workload: str):
+    """traffic_bytes_per_launch from a summary written by `traffic`, or None when the
+    summary is missing, names another workload, or predates the current kernel sources."""
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    kv = {}
+    for line in text.splitlines():
+        if ":" in line and not line.startswith(("#", "|", "-")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("--title", default="")
+    t.add_argument("--command", required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch_dir")
+    f.add_argument("write_dir")
+    f.add_argument("--copy-bytes", type=int, required=True)
+    f.add_argument("--workload", required=True)
+    f.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    {"trace": cmd_trace, "traffic": cmd_traffic}[a.cmd](a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -141,6 +141,47 @@ def illcond_spectrum(seed: int, j: int, k: int) -> np.ndarray:
     return 10.0 ** rng.uniform(-4.0, 0.0, size=k)
 
 
+def illcond_factors(wl: Workload, j: int):
+    """(U, s, V) with G_j = U diag(s) V^T before the float32 rounding (kind "illcond")."""
+    rows, cols = wl.shapes[j]
+    k = min(rows, cols)
+    u = _orthonormal_columns(wl.seed, j, _TID_U, rows, k)
+    v = _orthonormal_columns(wl.seed, j, _TID_V, cols, k)
+    return u, illcond_spectrum(wl.seed, j, k), v
+
+
+def illcond_inputs_device(wl: Workload, j: int, device):
+    """Inputs of matrix j of an "illcond" workload, built on `device`.
+
+    Same recipe as `matrix_inputs` (the same seeded float32 Gaussians, QR with
+    the signs of diag(R) fixed, s log-uniform on [1e-4, 1]), with the QR and
+    U diag(s) V^T done in float64 on the device, which is much faster for
+    6144-sided matrices.  The bits differ from the host version's, so a caller
+    checks against the oracle by copying these tensors back.  Returns
+    ({"w", "m", "g"} in the working dtype, (U, s, V) float64 on the device).
+    """
+    import torch
+
+    rows, cols = wl.shapes[j]
+    k = min(rows, cols)
+
+    def ortho(tid, n):
+        a = torch.from_numpy(_normal(wl.seed, j, tid, (n, k), 1.0)).to(device, torch.float64)
+        q, r = torch.linalg.qr(a)
+        d = torch.sign(torch.diagonal(r))
+        d[d == 0] = 1.0
+        return q * d
+
+    u = ortho(_TID_U, rows)
+    v = ortho(_TID_V, cols)
+    s = torch.from_numpy(illcond_spectrum(wl.seed, j, k)).to(device, torch.float64)
+    g = torch.matmul(u * s, v.t().contiguous()).to(torch.float32)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    w = cast(_normal(wl.seed, j, _TID_W, (rows, cols), wl.std_w), wl.dtype).to(device)
+    ins = {"w": w, "m": torch.zeros((rows, cols), dtype=tdt, device=device), "g": g.to(tdt)}
+    return ins, (u, s, v)
+
+
 def matrix_inputs(wl: Workload, j: int) -> Dict[str, np.ndarray]:
     """Inputs of matrix j of workload `wl`, as float32 arrays before the dtype cast."""
     rows, cols = wl.shapes[j]
@@ -152,10 +193,7 @@ def matrix_inputs(wl: Workload, j: int) -> Dict[str, np.ndarray]:
         g = _normal(wl.seed, j, _TID_G, (rows, cols), wl.std_g)
         return {"w": w, "m": m, "g": g}
     if wl.kind == "illcond":
-        k = min(rows, cols)
-        u = _orthonormal_columns(wl.seed, j, _TID_U, rows, k)
-        v = _orthonormal_columns(wl.seed, j, _TID_V, cols, k)
-        s = illcond_spectrum(wl.seed, j, k)
+        u, s, v = illcond_factors(wl, j)
         g = ((u * s) @ v.T).astype(np.float32)
         return {"w": w, "m": np.zeros((rows, cols), np.float32), "g": g}
     raise ValueError(f"unknown workload kind {wl.kind!r}")
