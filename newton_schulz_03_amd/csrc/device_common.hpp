@@ -102,14 +102,23 @@ __device__ __forceinline__ F block_sum(F v, F* scratch /* kThreads/64 entries */
   return t;
 }
 
-// Index j with prefix[j] <= b < prefix[j+1] (prefix is non-decreasing, prefix[0] = 0).
-__device__ __forceinline__ int find_matrix(const int32_t* prefix, int batch, int32_t b) {
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (prefix[mid] <= b) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+// The ping-pong iterate buffer `which` (0 or 1) of a matrix.  A select rather
+// than an index, so that a descriptor held by a kernel stays in registers.
+__device__ __forceinline__ void* iterate(const MatDesc& d, int which) {
+  return which ? d.x[1] : d.x[0];
+}
+
+// Index j with prefix[j] <= b < prefix[j+1], found by the whole block at once:
+// every thread tests a few intervals in parallel (one round of independent
+// loads) and the owner publishes j through `slot` in LDS.  Replaces a binary
+// search's chain of dependent loads at the start of every block.  Exactly one
+// interval holds b when b < prefix[batch]; empty intervals never match.
+__device__ __forceinline__ int locate_matrix(const int32_t* prefix, int batch, int32_t b,
+                                             int* slot) {
+  for (int k = threadIdx.x; k < batch; k += blockDim.x)
+    if (prefix[k] <= b && b < prefix[k + 1]) *slot = k;
+  __syncthreads();
+  return *slot;
 }
 
 // Slab layout of every workspace matrix (the iterate X, A and B): a padded

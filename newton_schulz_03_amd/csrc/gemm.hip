@@ -122,11 +122,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   constexpr int BK = kRowBytes / sizeof(T);
 
-  const TileRef tr = decode_tile<MODE>(c);
+  __shared__ int slot;
+  const TileRef tr = decode_tile<MODE>(c, &slot);
   const MatDesc& d = tr.d;
   const int32_t ti = tr.ti, tj = tr.tj;
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
-  const T* Xc = static_cast<const T*>(d.x[g.cur]);
+  const T* Xc = static_cast<const T*>(iterate(d, g.cur));
 
   // Operand P (MFMA rows, index p) and Q (MFMA columns, index q): D[p][q] = sum_k P[p][k] Q[q][k].
   // p_at / q_at: first row (K-major) or first column (MN-major) of the tile's operand.

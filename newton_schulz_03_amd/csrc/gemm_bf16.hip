@@ -196,7 +196,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
     uint16_t* dst;
     int64_t ld, r0, c0;
     if constexpr (MODE == GM_PROD) {
-      dst = static_cast<uint16_t*>(tr.d.x[g.cur ^ 1]);
+      dst = static_cast<uint16_t*>(iterate(tr.d, g.cur ^ 1));
       ld = tr.d.l_pad;
       r0 = static_cast<int64_t>(tr.ti) * kTile;
       c0 = static_cast<int64_t>(tr.tj) * kTile;
@@ -252,10 +252,11 @@ template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDSB];
 
-  const TileRef tr = decode_tile<MODE>(c);
+  __shared__ int slot;
+  const TileRef tr = decode_tile<MODE>(c, &slot);
   const MatDesc& d = tr.d;
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
-  const uint16_t* Xc = static_cast<const uint16_t*>(d.x[g.cur]);
+  const uint16_t* Xc = static_cast<const uint16_t*>(iterate(d, g.cur));
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -77,12 +77,14 @@ struct TileRef {
   int32_t ti, tj;
 };
 
-// Block -> (matrix, tile) for the symmetric phases (GRAM, POLY) or the product.
+// Block -> (matrix, tile) for the symmetric phases (GRAM, POLY) or the product,
+// with blocks renumbered XCD by XCD.  Called by the whole block: the matrix is
+// located cooperatively, through `slot` in LDS.
 template <int MODE>
-__device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c) {
+__device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int* slot) {
   const int32_t b = xcd_remap(static_cast<int32_t>(blockIdx.x), static_cast<int32_t>(gridDim.x));
   const int32_t* pre = c.prefix + (MODE == GM_PROD ? PH_PROD : PH_SYM) * (c.batch + 1);
-  const int j = find_matrix(pre, c.batch, b);
+  const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;
   r.d = c.desc[j];
   const int32_t t = b - pre[j];
@@ -132,8 +134,8 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
   const LanePos lp = lane_pos(tr);
   const int64_t s_pad = tr.d.s_pad, l_pad = tr.d.l_pad;
   if constexpr (MODE == GM_PROD) {
-    const T* __restrict__ xin = static_cast<const T*>(tr.d.x[g.cur]);
-    T* __restrict__ xout = static_cast<T*>(tr.d.x[g.cur ^ 1]);
+    const T* __restrict__ xin = static_cast<const T*>(iterate(tr.d, g.cur));
+    T* __restrict__ xout = static_cast<T*>(iterate(tr.d, g.cur ^ 1));
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       float x[4][4][4];

@@ -42,6 +42,7 @@ struct Plan {
   std::vector<int32_t> prefix;      // NPHASE x (batch + 1)
   int32_t totals[NPHASE] = {0, 0, 0, 0, 0};
   size_t table_bytes = 0;
+  size_t inv_off = 0;
   size_t partials_off = 0;
   size_t total_bytes = 0;
 };
@@ -104,6 +105,8 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
   off += align_up(sizeof(MatDesc) * batch, kAlign);
   off += align_up(sizeof(int32_t) * pl.prefix.size(), kAlign);
   pl.table_bytes = off;
+  pl.inv_off = off;
+  off += align_up(sizeof(float) * static_cast<size_t>(batch), kAlign);
   pl.partials_off = off;
   off += align_up(sizeof(float) * static_cast<size_t>(tot[PH_REDUCE]), kAlign);
   for (int32_t i = 0; i < batch; ++i) {
@@ -277,6 +280,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   c.desc = reinterpret_cast<const MatDesc*>(ws);
   c.prefix = reinterpret_cast<const int32_t*>(ws + align_up(sizeof(MatDesc) * pl.batch, kAlign));
   c.partials = reinterpret_cast<float*>(ws + pl.partials_off);
+  c.inv_norm = reinterpret_cast<float*>(ws + pl.inv_off);
   c.batch = pl.batch;
   c.stream = stream;
   hipError_t e;
@@ -288,6 +292,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   }
   {
     TimedLaunch t(MUON_K_NORMALIZE, stream);
+    if ((e = launch_finalize(c, ep)) != hipSuccess) return hip_fail(e, "launch norm finalize");
     if ((e = launch_normalize(c, pl.totals[PH_NORMALIZE], pl.bf16, ep)) != hipSuccess)
       return hip_fail(e, "launch normalize");
     t.done();

@@ -2,6 +2,7 @@
 //
 // Workspace layout, per call (offsets from the caller's 256-byte aligned base):
 //   [table]     MatDesc[batch], then the phase prefix arrays int32[NPHASE][batch+1]
+//   [inv]       float[batch]: 1 / (||U||_F + eps) per matrix
 //   [partials]  float[reduce blocks]: per-block sums of squares (Frobenius norm)
 //   per matrix  X ping, X pong: s_pad x l_pad;  A (Gram), B (polynomial): s_pad x s_pad
 // Every matrix is held in its wide orientation (short side first): a matrix
@@ -46,6 +47,7 @@ struct LaunchCtx {
   const MatDesc* desc;     // device copy of the descriptors
   const int32_t* prefix;   // device: NPHASE arrays of batch+1 block prefixes
   float* partials;         // device: per reduce-block sums of squares
+  float* inv_norm;         // device: per matrix 1 / (||U||_F + eps)
   int32_t batch;
   hipStream_t stream;
 };
@@ -61,6 +63,9 @@ struct ElemParams {
 
 // Host launchers (one per kernel family).  is_bf16 selects the element type.
 hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
+// One block per matrix: 1 / (||U||_F + eps) from the reduce partials, summed in a
+// fixed order in double.
+hipError_t launch_finalize(const LaunchCtx& c, const ElemParams& p);
 hipError_t launch_normalize(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 hipError_t launch_finish(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 // A = out_scale * X X^T  (out_scale = b when the polynomial has no A^2 term, else 1)

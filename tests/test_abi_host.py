@@ -48,6 +48,7 @@ def expected_workspace(shapes, esize):
     batch = len(shapes)
     desc = 112  # sizeof(MatDesc)
     total = up(desc * batch, 256) + up(4 * 5 * (batch + 1), 256)
+    total += up(4 * batch, 256)  # per-matrix 1 / (||U|| + eps)
     vec = 16 // esize
     blocks = sum(-(-r * c // (256 * vec * 8)) for r, c in shapes)
     total += up(4 * blocks, 256)
