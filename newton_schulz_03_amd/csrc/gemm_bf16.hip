@@ -13,7 +13,7 @@
 //    K-major operand (rows of X, A or B) is one contiguous 16 KiB slab and each
 //    load instruction reads 1 KiB of consecutive bytes.  In LDS the slab keeps
 //    its 64-byte rows, their four 16-byte chunks XOR-swizzled by
-//    ((row >> 1) ^ (row >> 3)) & 3 so that the fragment reads do not collide.
+//    ((row >> 2) ^ (row >> 3)) & 3 so that the fragment reads do not collide.
 //  * The MN-major operand of the product (X read along its columns) arrives as
 //    8 pieces of 32 rows x 64 bytes (one per slab), chunks swizzled by
 //    2 ((row >> 1) & 1); fragments are assembled with ds_read_b64_tr_b16, whose
@@ -39,7 +39,11 @@ static_assert(LDSB >= kTile * MNROW, "the tile store stages a whole 256 x 256 bf
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-__device__ __forceinline__ int kkey(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// Chunk key of a K-major LDS row.  It depends on row bits 2 and 3 only: with a
+// key that varies with bit 1, gfx950 serves the fragment reads (ds_read_b128,
+// lane l -> row l % 32) at half rate (measured with SQ_LDS_BANK_CONFLICT).
+// Rows 32 x + r share the key of r, which the fragment offsets rely on.
+__device__ __forceinline__ int kkey(int row) { return ((row >> 2) ^ (row >> 3)) & 3; }
 
 // s_waitcnt on vmcnt only (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
 template <int N>
