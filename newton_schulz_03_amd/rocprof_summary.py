@@ -33,7 +33,7 @@ KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_com
 
 SHORT_NAMES = (("k_gemm_bf16<0>", "gram"), ("k_gemm_bf16<1>", "poly"), ("k_gemm_bf16<2>", "prod"),
                ("k_gemm_staged", "gemm_fp32"), ("k_reduce", "reduce"), ("k_normalize", "normalize"),
-               ("k_finish", "finish"))
+               ("k_finish", "finish"), ("k_finalize", "finalize"))
 
 
 def kernel_source_digest() -> str:
