@@ -107,6 +107,104 @@ def cpu_baseline(wl, seconds: float, max_sample: int):
                       f"in float64 numpy, {dt:.1f} s of oracle time", "seconds": round(dt, 2)}
 
 
+def adamw_bytes_per_element(dtype: str) -> int:
+    """Algorithmic HBM bytes of one AdamW element: read p, g, m, v; write p, m, v."""
+    e = 2 if dtype == "bf16" else 4
+    return 3 * e + 4 * 4
+
+
+def bench_adamw(args, wl) -> int:
+    """One AdamW step per timed step over the workload's tensors (all resident in HBM)."""
+    import concurrent.futures
+
+    import torch
+
+    import newton_schulz_03_amd as nsa
+    import workloads
+
+    dev = torch.device("cuda:0")
+
+    def one(j):
+        raw = workloads.adamw_inputs(wl, j)
+        return j, {"p": workloads.cast(raw["p"], wl.dtype), "g": workloads.cast(raw["g"], wl.dtype),
+                   "m": torch.from_numpy(raw["m"]), "v": torch.from_numpy(raw["v"])}
+
+    print(f"[bench] generating {wl.name}: {wl.batch} tensors", file=sys.stderr, flush=True)
+    ins = [None] * wl.batch
+    with concurrent.futures.ThreadPoolExecutor(max_workers=16) as ex:
+        for j, d in ex.map(one, range(wl.batch)):
+            ins[j] = {k: v.to(dev) for k, v in d.items()}
+    torch.cuda.synchronize(dev)
+    P, G, M, V = ([d[k] for d in ins] for k in "pgmv")
+    ws_bytes = nsa.adamw_workspace_bytes(wl.numels)
+    raw_ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    off = (-raw_ws.data_ptr()) % 256
+    ws = raw_ws[off:off + ws_bytes]
+
+    def step():
+        nsa.adamw_batched(P, G, M, V, lr=wl.lr, betas=(wl.beta1, wl.beta2), eps=wl.eps,
+                          weight_decay=wl.weight_decay, step=wl.step, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    nsa.timing_reset()
+    nsa.timing_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize(dev)
+    nsa.timing_enable(False)
+    kern = nsa.timing_read()
+    total_ms = start.elapsed_time(end)
+    n = sum(wl.numels)
+    bpe = adamw_bytes_per_element(wl.dtype)
+    k_ms = kern["adamw"][0] / max(1, kern["adamw"][1])
+    gbs = n * bpe / (k_ms * 1e-3) / 1e9
+    result = {
+        "metric": "AdamW parameters updated/sec (non-expert parameters)",
+        "value": round(n * args.steps / (total_ms * 1e-3), 1),
+        "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "tensors": wl.batch, "elements": n,
+                   "moments": "fp32", "lr": wl.lr, "betas": [wl.beta1, wl.beta2],
+                   "weight_decay": wl.weight_decay, "step": wl.step},
+        "roofline": {"bound": "hbm", "kernel": "adamw", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_element": bpe},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+
+        print(f"[bench] timing the oracle for about {args.cpu_seconds:.0f} s", file=sys.stderr,
+              flush=True)
+        done, dt, j = 0, 0.0, 0
+        while dt < args.cpu_seconds and j < wl.batch:
+            raw = workloads.adamw_inputs(wl, j)
+            h = {k: workloads.as_float64(workloads.cast(v, wl.dtype)) if k in "pg" else
+                 raw[k].astype(np.float64) for k, v in raw.items()}
+            t0 = time.perf_counter()
+            oracle.adamw_step(h["p"], h["g"], h["m"], h["v"], lr=wl.lr, beta1=wl.beta1,
+                              beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay,
+                              step=wl.step)
+            dt += time.perf_counter() - t0
+            done += wl.numels[j]
+            j += 1
+        result["cpu_baseline"] = {"value": round(done / dt, 1), "unit": "elements/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"first {j} of {wl.batch} tensors ({done} elements), "
+                                            f"float64 numpy, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +237,9 @@ def main(argv=None) -> int:
     nsa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    adamw = workloads.adamw_workloads()
+    if args.workload in adamw:
+        return bench_adamw(args, adamw[args.workload])
     wl = workloads.standard_workloads()[args.workload]
     print(f"[bench] generating {wl.name}: {wl.batch} matrices", file=sys.stderr, flush=True)
     t0 = time.time()

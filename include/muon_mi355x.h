@@ -128,6 +128,51 @@ int32_t muon_step_batched(int32_t batch, const int64_t* rows, const int64_t* col
                           const muon_step_params* p, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * AdamW for the parameters Muon does not cover.  The model runs Muon on about
+ * 99.5% of its parameters and AdamW on the rest ("Domyn is training a
+ * 1T-parameter MoE on Europe's Jupiter supercomputer, and published the
+ * recipe", §The model and the machine, optimizer row).  The pages do not spell
+ * AdamW out; this is Adam with decoupled weight decay in the form PyTorch's
+ * AdamW takes, for step number t >= 1 (the step being taken):
+ *     p <- p * (1 - lr * weight_decay)
+ *     m <- beta1 * m + (1 - beta1) * g
+ *     v <- beta2 * v + (1 - beta2) * g^2
+ *     p <- p - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * The arithmetic is fp32; the bias corrections are formed on the host in double.
+ */
+typedef struct {
+  float lr;
+  float beta1, beta2;     /* each in [0, 1) */
+  float eps;              /* >= 0 */
+  float weight_decay;
+  int32_t step;           /* t >= 1 */
+} muon_adamw_params;
+
+/*
+ * Bytes of device workspace muon_adamw_batched needs for this batch (the
+ * descriptor table).  numel[i] >= 0: element count of tensor i.  Returns
+ * SIZE_MAX on invalid arguments.  Host-only.
+ */
+size_t muon_adamw_workspace_bytes(int32_t batch, const int64_t* numel);
+
+/*
+ * One AdamW step over a ragged batch of flat tensors, in place.
+ *   numel[i]   element count of tensor i (0 allowed: nothing to do)
+ *   p[i], g[i] parameters and gradients, `dtype` elements (MUON_BF16 or MUON_FP32);
+ *              p is updated in place, g is read only
+ *   m[i], v[i] first and second moments, always fp32, updated in place
+ *   workspace  device buffer of at least muon_adamw_workspace_bytes() bytes,
+ *              256-byte aligned
+ * Device pointers must be 16-byte aligned device memory; p, g, m and v of one
+ * tensor must be distinct.  Conventions (ownership, stream, validation before
+ * any launch, status codes) are those listed at the top of this header.
+ */
+int32_t muon_adamw_batched(int32_t batch, const int64_t* numel, void* const* p,
+                           const void* const* g, float* const* m, float* const* v, int32_t dtype,
+                           const muon_adamw_params* params, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Kernels of the step, for per-kernel timing. */
 typedef enum {
   MUON_K_REDUCE = 0,    /* momentum and per-block sums of squares */
@@ -136,7 +181,8 @@ typedef enum {
   MUON_K_POLY = 3,      /* B = b A + c A^2 */
   MUON_K_PROD = 4,      /* X <- a X + B X */
   MUON_K_FINISH = 5,    /* W update, or the output copy */
-  MUON_K_COUNT = 6
+  MUON_K_ADAMW = 6,     /* muon_adamw_batched */
+  MUON_K_COUNT = 7
 } muon_kernel;
 
 /*

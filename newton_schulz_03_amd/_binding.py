@@ -23,9 +23,10 @@ QUINTIC = (3.4445, -4.7750, 2.0315)
 CUBIC = (1.5, -0.5, 0.0)
 
 EXPORTED = ("muon_workspace_bytes", "muon_ns_batched", "muon_step_batched",
+            "muon_adamw_workspace_bytes", "muon_adamw_batched",
             "muon_status_string", "muon_last_error_detail", "muon_timing_enable",
             "muon_timing_read", "muon_timing_reset")
-KERNELS = ("reduce", "normalize", "gram", "poly", "prod", "finish")
+KERNELS = ("reduce", "normalize", "gram", "poly", "prod", "finish", "adamw")
 
 
 class MuonError(RuntimeError):
@@ -44,6 +45,12 @@ class NsParams(ctypes.Structure):
 class StepParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta", ctypes.c_float), ("nesterov", ctypes.c_int32),
                 ("ns", NsParams)]
+
+
+class AdamWParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int32)]
 
 
 _lib_handle: Optional[ctypes.CDLL] = None
@@ -69,6 +76,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_step_batched.argtypes = [i32, i64p, i64p, vpp, vpp, vpp, i32,
                                       ctypes.POINTER(StepParams), vp, sz, vp]
     lib.muon_step_batched.restype = i32
+    lib.muon_adamw_workspace_bytes.argtypes = [i32, i64p]
+    lib.muon_adamw_workspace_bytes.restype = sz
+    lib.muon_adamw_batched.argtypes = [i32, i64p, vpp, vpp, vpp, vpp, i32,
+                                       ctypes.POINTER(AdamWParams), vp, sz, vp]
+    lib.muon_adamw_batched.restype = i32
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error_detail.argtypes = []
@@ -227,6 +239,64 @@ def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, bet
                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                    ctypes.c_void_p(_stream_handle(dev)))
     _check(st, "muon_step_batched")
+
+
+def adamw_workspace_bytes(numels: Sequence[int]) -> int:
+    lib = load_library()
+    numels = list(numels)
+    n = lib.muon_adamw_workspace_bytes(len(numels), _i64_array(numels) if numels else None)
+    if n == SIZE_MAX:
+        raise MuonError(MUON_ERR_INVALID_ARG, "muon_adamw_workspace_bytes", last_error_detail())
+    return n
+
+
+def adamw_batched(params: Sequence, grads: Sequence, exp_avgs: Sequence, exp_avg_sqs: Sequence,
+                  lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
+                  weight_decay: float = 1e-2, step: int = 1, workspace=None) -> None:
+    """One AdamW step over a ragged batch of tensors, in place on params and the moments.
+
+    params/grads: bf16 or fp32 (one dtype for all), contiguous; exp_avgs and
+    exp_avg_sqs: fp32, same shapes.  `step` is the number of the step being
+    taken (1 for the first).  Runs on the current HIP stream.
+    """
+    import torch
+
+    lib = load_library()
+    ps, gs, ms, vs = list(params), list(grads), list(exp_avgs), list(exp_avg_sqs)
+    if not ps:
+        return
+    if not (len(ps) == len(gs) == len(ms) == len(vs)):
+        raise ValueError("params, grads and moments must have one tensor each per entry")
+    dev = ps[0].device
+    if dev.type != "cuda":
+        raise ValueError(f"params must live on a HIP device, got {dev}")
+    for group, want in ((ps, ps[0].dtype), (gs, ps[0].dtype), (ms, torch.float32),
+                        (vs, torch.float32)):
+        for t in group:
+            if t.device != dev or t.dtype != want or not t.is_contiguous():
+                raise ValueError("tensors must be contiguous on one device; p and g share a "
+                                 "dtype, the moments are float32")
+    for p, g, m, v in zip(ps, gs, ms, vs):
+        if not (p.shape == g.shape == m.shape == v.shape):
+            raise ValueError("p, g, m and v of one entry must have the same shape")
+    code = _dtype_code(ps[0].dtype)
+    numels = [p.numel() for p in ps]
+    if workspace is None:
+        n = adamw_workspace_bytes(numels)
+        ws = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device=dev)
+        off = (-ws.data_ptr()) % 256
+        workspace = ws[off:off + max(n, 1)]
+    b1, b2 = (float(b) for b in betas)
+    prm = AdamWParams(float(lr), b1, b2, float(eps), float(weight_decay), int(step))
+    with torch.cuda.device(dev):
+        st = lib.muon_adamw_batched(len(ps), _i64_array(numels),
+                                    _ptr_array([t.data_ptr() for t in ps]),
+                                    _ptr_array([t.data_ptr() for t in gs]),
+                                    _ptr_array([t.data_ptr() for t in ms]),
+                                    _ptr_array([t.data_ptr() for t in vs]), code,
+                                    ctypes.byref(prm), ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel(), ctypes.c_void_p(_stream_handle(dev)))
+    _check(st, "muon_adamw_batched")
 
 
 def timing_enable(on: bool = True) -> None:

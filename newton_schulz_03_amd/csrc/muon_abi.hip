@@ -155,7 +155,9 @@ int32_t hip_fail(hipError_t e, const char* what) {
   return fail(MUON_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
 }
 
-int32_t upload_table(const Plan& pl, void* ws, hipStream_t stream) {
+// Copies `bytes` composed by `fill` into a pinned slot, then to `dst` on `stream`.
+template <typename Fill>
+int32_t stage_upload(size_t bytes, Fill fill, void* dst, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -172,25 +174,64 @@ int32_t upload_table(const Plan& pl, void* ws, hipStream_t stream) {
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging slot)");
     s.pending = false;
   }
-  if (s.cap < pl.table_bytes) {
+  if (s.cap < bytes) {
     if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
     s.cap = 0;
-    const size_t cap = std::max<size_t>(pl.table_bytes, 64 * 1024);
+    const size_t cap = std::max<size_t>(bytes, 64 * 1024);
     e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
     s.cap = cap;
   }
   char* h = static_cast<char*>(s.host);
-  std::memset(h, 0, pl.table_bytes);
-  std::memcpy(h, pl.desc.data(), sizeof(MatDesc) * pl.batch);
-  std::memcpy(h + align_up(sizeof(MatDesc) * pl.batch, kAlign), pl.prefix.data(),
-              sizeof(int32_t) * pl.prefix.size());
-  e = hipMemcpyAsync(ws, h, pl.table_bytes, hipMemcpyHostToDevice, stream);
+  std::memset(h, 0, bytes);
+  fill(h);
+  e = hipMemcpyAsync(dst, h, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (descriptor table)");
   e = hipEventRecord(s.done, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   s.pending = true;
+  return MUON_OK;
+}
+
+int32_t upload_table(const Plan& pl, void* ws, hipStream_t stream) {
+  return stage_upload(
+      pl.table_bytes,
+      [&](char* h) {
+        std::memcpy(h, pl.desc.data(), sizeof(MatDesc) * pl.batch);
+        std::memcpy(h + align_up(sizeof(MatDesc) * pl.batch, kAlign), pl.prefix.data(),
+                    sizeof(int32_t) * pl.prefix.size());
+      },
+      ws, stream);
+}
+
+// AdamW: descriptors, then the block prefix array.
+struct AdamPlan {
+  int32_t batch = 0;
+  bool bf16 = true;
+  std::vector<AdamDesc> desc;
+  std::vector<int32_t> prefix;
+  size_t prefix_off = 0;
+  size_t total_bytes = 0;
+};
+
+int32_t make_adam_plan(int32_t batch, const int64_t* numel, AdamPlan& pl) {
+  if (batch < 0) return fail(MUON_ERR_INVALID_ARG, "batch = %d is negative", batch);
+  if (batch > 0 && numel == nullptr) return fail(MUON_ERR_INVALID_ARG, "numel array is null");
+  pl.batch = batch;
+  pl.desc.assign(batch, AdamDesc{});
+  pl.prefix.assign(batch + 1, 0);
+  int64_t total = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    if (numel[i] < 0) return fail(MUON_ERR_INVALID_ARG, "tensor %d: numel %lld is negative", i,
+                                  static_cast<long long>(numel[i]));
+    pl.desc[i].numel = numel[i];
+    total += adamw_blocks(numel[i]);
+    if (total > INT32_MAX) return fail(MUON_ERR_UNSUPPORTED, "batch needs more than 2^31 blocks");
+    pl.prefix[i + 1] = static_cast<int32_t>(total);
+  }
+  pl.prefix_off = align_up(sizeof(AdamDesc) * batch, kAlign);
+  pl.total_bytes = batch == 0 ? 0 : pl.prefix_off + align_up(sizeof(int32_t) * (batch + 1), kAlign);
   return MUON_OK;
 }
 
@@ -203,8 +244,8 @@ std::mutex g_timing_mu;
 bool g_timing_on = false;
 std::vector<hipEvent_t> g_event_pool;
 std::vector<TimingRec> g_pending;
-double g_total_ms[MUON_K_COUNT] = {0, 0, 0, 0, 0, 0};
-int64_t g_launches[MUON_K_COUNT] = {0, 0, 0, 0, 0, 0};
+double g_total_ms[MUON_K_COUNT] = {};
+int64_t g_launches[MUON_K_COUNT] = {};
 
 hipEvent_t take_event() {
   if (!g_event_pool.empty()) {
@@ -424,6 +465,93 @@ extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const i
     ep.eps = p->ns.eps;
     ep.lr = p->lr;
     return run(pl, ws, s, ep, p->ns);
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "unexpected host exception");
+  }
+}
+
+extern "C" size_t muon_adamw_workspace_bytes(int32_t batch, const int64_t* numel) {
+  g_detail.clear();
+  AdamPlan pl;
+  if (make_adam_plan(batch, numel, pl) != MUON_OK) return SIZE_MAX;
+  return pl.total_bytes;
+}
+
+extern "C" int32_t muon_adamw_batched(int32_t batch, const int64_t* numel, void* const* p,
+                                      const void* const* g, float* const* m, float* const* v,
+                                      int32_t dtype, const muon_adamw_params* prm,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    g_detail.clear();
+    AdamPlan pl;
+    int32_t st = make_adam_plan(batch, numel, pl);
+    if (st != MUON_OK) return st;
+    if (dtype != MUON_BF16 && dtype != MUON_FP32)
+      return fail(MUON_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    pl.bf16 = dtype == MUON_BF16;
+    if (prm == nullptr) return fail(MUON_ERR_INVALID_ARG, "params pointer is null");
+    if (!std::isfinite(prm->lr) || !std::isfinite(prm->weight_decay) || !std::isfinite(prm->eps) ||
+        prm->eps < 0.f)
+      return fail(MUON_ERR_INVALID_ARG, "lr, weight_decay must be finite and eps finite and >= 0");
+    if (!(prm->beta1 >= 0.f && prm->beta1 < 1.f) || !(prm->beta2 >= 0.f && prm->beta2 < 1.f))
+      return fail(MUON_ERR_INVALID_ARG, "beta1 and beta2 must lie in [0, 1)");
+    if (prm->step < 1) return fail(MUON_ERR_INVALID_ARG, "step = %d: must be >= 1", prm->step);
+    if (batch == 0) return MUON_OK;
+    if (p == nullptr || g == nullptr || m == nullptr || v == nullptr)
+      return fail(MUON_ERR_INVALID_ARG, "p/g/m/v array is null");
+    for (int32_t i = 0; i < batch; ++i) {
+      if (numel[i] == 0) continue;
+      const void* q[4] = {p[i], g[i], m[i], v[i]};
+      for (int k = 0; k < 4; ++k) {
+        if (q[k] == nullptr) return fail(MUON_ERR_INVALID_ARG, "tensor %d: null device pointer", i);
+        if (!aligned16(q[k]))
+          return fail(MUON_ERR_INVALID_ARG, "tensor %d: device pointer not 16-byte aligned", i);
+        for (int l = 0; l < k; ++l)
+          if (q[k] == q[l])
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: p, g, m and v must be distinct", i);
+      }
+      pl.desc[i].p = p[i];
+      pl.desc[i].g = g[i];
+      pl.desc[i].m = m[i];
+      pl.desc[i].v = v[i];
+    }
+    if (workspace == nullptr || workspace_bytes < pl.total_bytes)
+      return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                  pl.total_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+      return fail(MUON_ERR_INVALID_ARG, "workspace not %d-byte aligned", kAlign);
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = stage_upload(
+        pl.total_bytes,
+        [&](char* h) {
+          std::memcpy(h, pl.desc.data(), sizeof(AdamDesc) * pl.batch);
+          std::memcpy(h + pl.prefix_off, pl.prefix.data(), sizeof(int32_t) * pl.prefix.size());
+        },
+        ws, s);
+    if (st != MUON_OK) return st;
+    const double t = static_cast<double>(prm->step);
+    const double bc1 = 1.0 - std::pow(static_cast<double>(prm->beta1), t);
+    const double bc2 = 1.0 - std::pow(static_cast<double>(prm->beta2), t);
+    AdamParams a{};
+    a.decay = static_cast<float>(1.0 - static_cast<double>(prm->lr) * prm->weight_decay);
+    a.beta1 = prm->beta1;
+    a.one_minus_beta1 = static_cast<float>(1.0 - prm->beta1);
+    a.beta2 = prm->beta2;
+    a.one_minus_beta2 = static_cast<float>(1.0 - prm->beta2);
+    a.step_size = static_cast<float>(prm->lr / bc1);
+    a.inv_bc2_sqrt = static_cast<float>(1.0 / std::sqrt(bc2));
+    a.eps = prm->eps;
+    AdamCtx c{};
+    c.desc = reinterpret_cast<const AdamDesc*>(ws);
+    c.prefix = reinterpret_cast<const int32_t*>(ws + pl.prefix_off);
+    c.batch = pl.batch;
+    c.stream = s;
+    TimedLaunch tl(MUON_K_ADAMW, s);
+    hipError_t e = launch_adamw(c, pl.prefix[pl.batch], pl.bf16, a);
+    if (e != hipSuccess) return hip_fail(e, "launch adamw");
+    tl.done();
+    return MUON_OK;
   } catch (...) {
     return fail(MUON_ERR_HIP, "unexpected host exception");
   }

@@ -61,6 +61,34 @@ struct ElemParams {
   int32_t cur;       // which X buffer holds the final iterate (finish)
 };
 
+// AdamW over a ragged batch of flat tensors.
+struct AdamDesc {
+  void* p;          // parameters (T), updated in place
+  const void* g;    // gradients (T)
+  float* m;         // first moment, fp32, updated in place
+  float* v;         // second moment, fp32, updated in place
+  int64_t numel;
+};
+
+struct AdamCtx {
+  const AdamDesc* desc;    // device copy of the descriptors
+  const int32_t* prefix;   // device: batch+1 block prefixes
+  int32_t batch;
+  hipStream_t stream;
+};
+
+struct AdamParams {
+  float decay;            // 1 - lr * weight_decay
+  float beta1, one_minus_beta1;
+  float beta2, one_minus_beta2;
+  float step_size;        // lr / (1 - beta1^t)
+  float inv_bc2_sqrt;     // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+
+int64_t adamw_blocks(int64_t numel);
+hipError_t launch_adamw(const AdamCtx& c, int32_t nblocks, bool is_bf16, const AdamParams& a);
+
 // Host launchers (one per kernel family).  is_bf16 selects the element type.
 hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 // One block per matrix: 1 / (||U||_F + eps) from the reduce partials, summed in a

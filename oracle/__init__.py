@@ -8,3 +8,4 @@ from .muon_oracle import (  # noqa: F401
     muon_step, muon_step_batched, nesterov_direction, newton_schulz, normalize,
     ns_batched, update_scale,
 )
+from .adamw_oracle import adamw_batched, adamw_step  # noqa: F401,E402

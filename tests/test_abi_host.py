@@ -127,3 +127,50 @@ def test_step_validation(lib):
     assert step_call(lib, steps=-2) == E.MUON_ERR_INVALID_ARG
     assert step_call(lib, g=0) == E.MUON_ERR_INVALID_ARG
     assert step_call(lib, ws_bytes=16) == E.MUON_ERR_WORKSPACE
+
+
+def adamw_call(lib, batch=1, numel=(100,), p=(FAKE,), g=(FAKE + 4096,), m=(FAKE + 8192,),
+               v=(FAKE + 12288,), dtype=0, lr=1e-3, b1=0.9, b2=0.95, eps=1e-8, wd=0.1, step=1,
+               ws=FAKE + (1 << 20), ws_bytes=1 << 40, params=True):
+    prm = nsa.AdamWParams(lr, b1, b2, eps, wd, step)
+    return lib.muon_adamw_batched(batch, _i64_array(numel) if numel is not None else None,
+                                  _ptr_array(p) if p is not None else None,
+                                  _ptr_array(g) if g is not None else None,
+                                  _ptr_array(m) if m is not None else None,
+                                  _ptr_array(v) if v is not None else None, dtype,
+                                  ctypes.byref(prm) if params else None, ctypes.c_void_p(ws),
+                                  ws_bytes, None)
+
+
+def test_adamw_workspace_bytes(lib):
+    def up(x, a):
+        return (x + a - 1) // a * a
+    for numels in [[1], [0, 5, 8192 * 4 + 1], [6144] * 223]:
+        b = len(numels)
+        assert nsa.adamw_workspace_bytes(numels) == up(40 * b, 256) + up(4 * (b + 1), 256)
+    assert nsa.adamw_workspace_bytes([]) == 0
+    assert lib.muon_adamw_workspace_bytes(1, _i64_array([-1])) == nsa._binding.SIZE_MAX
+    assert "negative" in nsa.last_error_detail()
+
+
+def test_adamw_validation(lib):
+    E = nsa
+    assert adamw_call(lib, batch=0, numel=None, p=None, g=None, m=None, v=None) == E.MUON_OK
+    assert adamw_call(lib, batch=-1) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, numel=(-4,)) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, dtype=3) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, step=0) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, b1=1.0) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, b2=-0.1) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, eps=-1.0) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, lr=float("nan")) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, params=False) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, p=None) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, v=(0,)) == E.MUON_ERR_INVALID_ARG
+    assert adamw_call(lib, m=(FAKE + 8,)) == E.MUON_ERR_INVALID_ARG
+    assert "aligned" in nsa.last_error_detail()
+    assert adamw_call(lib, g=(FAKE,)) == E.MUON_ERR_INVALID_ARG
+    assert "distinct" in nsa.last_error_detail()
+    assert adamw_call(lib, ws=0) == E.MUON_ERR_WORKSPACE
+    assert adamw_call(lib, ws_bytes=8) == E.MUON_ERR_WORKSPACE
+    assert adamw_call(lib, ws=FAKE + (1 << 20) + 16) == E.MUON_ERR_INVALID_ARG

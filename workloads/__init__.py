@@ -108,6 +108,62 @@ def standard_workloads() -> Dict[str, Workload]:
     }
 
 
+@dataclasses.dataclass(frozen=True)
+class AdamWWorkload:
+    """A ragged batch of flat tensors for the AdamW step.
+
+    p ~ N(0, std_p^2), g ~ N(0, std_g^2), m ~ N(0, std_m^2), v = (N(0, std_m))^2
+    (non-negative, as a second moment is); p and g in `dtype`, m and v fp32.
+    """
+
+    name: str
+    dtype: str
+    numels: Tuple[int, ...]
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.95
+    eps: float = 1e-8
+    weight_decay: float = 0.1
+    step: int = 10
+    std_p: float = 0.02
+    std_g: float = 1e-3
+    std_m: float = 1e-3
+    seed: int = 6
+
+    @property
+    def batch(self) -> int:
+        return len(self.numels)
+
+
+HIDDEN = 6144
+LAYERS = 74
+ROUTED_EXPERTS = 384
+
+
+def adamw_workloads() -> Dict[str, AdamWWorkload]:
+    """The non-expert parameters of the model, for AdamW: per layer two norm
+    weights (hidden size) and the router (routed experts x hidden), plus the
+    final norm; 175.5 M elements in 223 tensors."""
+    numels: List[int] = []
+    for _ in range(LAYERS):
+        numels += [HIDDEN, HIDDEN, ROUTED_EXPERTS * HIDDEN]
+    numels.append(HIDDEN)
+    return {
+        "adamw_nonexpert_74_layers": AdamWWorkload(
+            name="adamw_nonexpert_74_layers", dtype="bf16", numels=tuple(numels)),
+    }
+
+
+def adamw_inputs(wl: AdamWWorkload, j: int) -> Dict[str, np.ndarray]:
+    """Inputs of tensor j as float32 arrays (p and g before the dtype cast)."""
+    n = wl.numels[j]
+    m = _normal(wl.seed, j, _TID_M, (n,), wl.std_m)
+    v = _normal(wl.seed, j, _TID_V, (n,), wl.std_m)
+    return {"p": _normal(wl.seed, j, _TID_W, (n,), wl.std_p),
+            "g": _normal(wl.seed, j, _TID_G, (n,), wl.std_g),
+            "m": m, "v": v * v}
+
+
 def c1_cubic() -> Workload:
     """Workload 1 in its cubic mode: (a, b, c) = (1.5, -0.5, 0), 30 steps."""
     return dataclasses.replace(standard_workloads()["c1_fp32_256x512"],
