@@ -83,12 +83,25 @@ typedef struct {
   float eps;
 } muon_ns_params;
 
-/* Full step settings: learning rate, momentum coefficient, Nesterov flag (0/1). */
+/*
+ * Full step settings: learning rate, momentum coefficient, Nesterov flag (0/1),
+ * and where the momentum lives.
+ *
+ * momentum_host = 1 keeps the optimizer state in host memory, as the pages do
+ * when they move optimizer state off the accelerator ("Domyn is training a
+ * 1T-parameter MoE on Europe's Jupiter supercomputer, and published the
+ * recipe", §What moved the number, Offloading bullet).  Every m[i] must then be
+ * pinned host memory (hipHostMalloc, or a pinned torch tensor); the step reads
+ * M and writes the new momentum there in place, over the host link, once each,
+ * and works from a device copy kept in the workspace.  Otherwise (0) m[i] are
+ * device memory.
+ */
 typedef struct {
   float lr;
   float beta;
   int32_t nesterov;
   muon_ns_params ns;
+  int32_t momentum_host;
 } muon_step_params;
 
 /*

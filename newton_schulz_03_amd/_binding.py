@@ -44,7 +44,7 @@ class NsParams(ctypes.Structure):
 
 class StepParams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta", ctypes.c_float), ("nesterov", ctypes.c_int32),
-                ("ns", NsParams)]
+                ("ns", NsParams), ("momentum_host", ctypes.c_int32)]
 
 
 class AdamWParams(ctypes.Structure):
@@ -210,8 +210,12 @@ def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
 
 def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, beta: float = 0.95,
                  nesterov: bool = False, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
-                 workspace=None) -> None:
-    """One Muon step over a ragged batch, in place on ws (weights) and ms (momentum)."""
+                 workspace=None, momentum_host: bool = False) -> None:
+    """One Muon step over a ragged batch, in place on ws (weights) and ms (momentum).
+
+    momentum_host: the momenta are pinned host tensors (pin_memory), which the
+    GPU reads and writes in place over the host link.
+    """
     import torch
 
     lib = load_library()
@@ -220,7 +224,15 @@ def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, bet
         raise ValueError("ws, gs and ms must have the same length")
     if not ws:
         return
-    dev = _check_tensors(ws + gs + ms, "ws/gs/ms")
+    if momentum_host:
+        dev = _check_tensors(ws + gs, "ws/gs")
+        for m in ms:
+            if m.device.type != "cpu" or not m.is_pinned() or m.dtype != ws[0].dtype or \
+                    m.dim() != 2 or not m.is_contiguous():
+                raise ValueError("ms: with momentum_host, every momentum must be a pinned, "
+                                 "contiguous 2-D host tensor of the weights' dtype")
+    else:
+        dev = _check_tensors(ws + gs + ms, "ws/gs/ms")
     shapes = [tuple(w.shape) for w in ws]
     if any(tuple(g.shape) != s or tuple(m.shape) != s for g, m, s in zip(gs, ms, shapes)):
         raise ValueError("w, g and m of one matrix must share a shape")
@@ -228,8 +240,8 @@ def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, bet
     if workspace is None:
         workspace = allocate_workspace(shapes, ws[0].dtype, dev)
     a, b, c = (float(v) for v in coeffs)
-    p = StepParams(float(lr), float(beta), 1 if nesterov else 0, NsParams(int(steps), a, b, c,
-                                                                         float(eps)))
+    p = StepParams(float(lr), float(beta), 1 if nesterov else 0,
+                   NsParams(int(steps), a, b, c, float(eps)), 1 if momentum_host else 0)
     with torch.cuda.device(dev):
         st = lib.muon_step_batched(len(ws), _i64_array([s[0] for s in shapes]),
                                    _i64_array([s[1] for s in shapes]),

@@ -1,5 +1,6 @@
 // Bandwidth-bound kernels of the Muon step:
-//   k_reduce     momentum M' = beta*M + G (step) and per-block sums of U^2
+//   k_reduce     momentum M' = beta*M + G (step) and per-block sums of U^2; with the
+//                momentum in host memory it also leaves a device copy of the new momentum
 //   k_finalize   1 / (||U||_F + eps) per matrix from those partials
 //   k_normalize  X0 = U / (||U||_F + eps) in the wide orientation, zero padded
 //   k_finish     W' = W - lr*sqrt(max(1,rows/cols))*O (step) or out = O (orthogonalize only)
@@ -33,7 +34,7 @@ struct URow {
         if (p.mode == MODE_NS) {
           vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), o);
         } else {
-          vec_to_f32<T>(ld16(static_cast<const T*>(d.mom) + off), o);
+          vec_to_f32<T>(ld16(static_cast<const T*>(d.u_src) + off), o);
           if (p.nesterov) {
             float g[V];
             vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), g);
@@ -50,7 +51,7 @@ struct URow {
             if (p.mode == MODE_NS) {
               v = Elt<T>::to_f32(static_cast<const T*>(d.src)[off]);
             } else {
-              v = Elt<T>::to_f32(static_cast<const T*>(d.mom)[off]);
+              v = Elt<T>::to_f32(static_cast<const T*>(d.u_src)[off]);
               if (p.nesterov) v = Elt<T>::to_f32(static_cast<const T*>(d.src)[off]) + p.beta * v;
             }
           }
@@ -96,6 +97,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(LaunchCtx c, ElemParams p) 
       }
     } else {
       T* __restrict__ mom = static_cast<T*>(d.mom) + base;
+      T* __restrict__ copy = d.mom_copy ? static_cast<T*>(d.mom_copy) + base : nullptr;
       u32x4_t gv[kReduceIters], mv[kReduceIters];
 #pragma unroll
       for (int it = 0; it < kReduceIters; ++it) {
@@ -113,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(LaunchCtx c, ElemParams p) 
         for (int e = 0; e < V; ++e) mn[e] = p.beta * m[e] + g[e];
         const u32x4_t packed = f32_to_vec<T>(mn);
         st16(mom + off, packed);
+        if (copy) st16(copy + off, packed);
         vec_to_f32<T>(packed, mr);  // U is formed from the stored (rounded) M', as later kernels do
 #pragma unroll
         for (int e = 0; e < V; ++e) {
@@ -155,10 +158,14 @@ __global__ __launch_bounds__(kThreads) void k_reduce(LaunchCtx c, ElemParams p) 
         u32x4_t packed = f32_to_vec<T>(mn);
         float mr[V];
         vec_to_f32<T>(packed, mr);
+        T* cp = d.mom_copy ? static_cast<T*>(d.mom_copy) + off : nullptr;
         if (n == V) {
           st16(mp, packed);
+          if (cp) st16(cp, packed);
         } else {
           for (int e = 0; e < n; ++e) mp[e] = Elt<T>::from_f32(mn[e]);
+          if (cp)
+            for (int e = 0; e < n; ++e) cp[e] = Elt<T>::from_f32(mn[e]);
         }
 #pragma unroll
         for (int e = 0; e < V; ++e) u[e] = p.nesterov ? g[e] + p.beta * mr[e] : mr[e];

@@ -437,6 +437,8 @@ extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const i
       return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
     if (p->nesterov != 0 && p->nesterov != 1)
       return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
+    if (p->momentum_host != 0 && p->momentum_host != 1)
+      return fail(MUON_ERR_INVALID_ARG, "momentum_host must be 0 or 1");
     if (batch == 0) return MUON_OK;
     if (w == nullptr || g == nullptr || m == nullptr)
       return fail(MUON_ERR_INVALID_ARG, "w/g/m array is null");
@@ -453,8 +455,28 @@ extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const i
     bind(pl, ws);
     for (int32_t i = 0; i < batch; ++i) {
       pl.desc[i].src = g[i];
-      pl.desc[i].mom = m[i];
       pl.desc[i].dst = w[i];
+      if (p->momentum_host) {
+        // pinned host memory: the kernels use its device mapping, and the new
+        // momentum is also copied into the second iterate buffer, which nothing
+        // uses before the first product
+        hipPointerAttribute_t attr{};
+        hipError_t e = hipPointerGetAttributes(&attr, m[i]);
+        if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
+          (void)hipGetLastError();
+          return fail(MUON_ERR_INVALID_ARG,
+                      "matrix %d: momentum_host is set but m is not pinned host memory", i);
+        }
+        if (!aligned16(attr.devicePointer))
+          return fail(MUON_ERR_INVALID_ARG, "matrix %d: device mapping of m not 16-byte aligned", i);
+        pl.desc[i].mom = attr.devicePointer;
+        pl.desc[i].mom_copy = pl.desc[i].x[1];
+        pl.desc[i].u_src = pl.desc[i].x[1];
+      } else {
+        pl.desc[i].mom = m[i];
+        pl.desc[i].mom_copy = nullptr;
+        pl.desc[i].u_src = m[i];
+      }
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = upload_table(pl, ws, s)) != MUON_OK) return st;

@@ -41,6 +41,8 @@ struct MatDesc {
   int32_t vec_ok;             // cols is a multiple of the 16-byte vector width
   float scale;                // sqrt(max(1, rows/cols))
   int32_t reserved;
+  const void* u_src;          // STEP: where later kernels read the new momentum (mom, or mom_copy)
+  void* mom_copy;             // STEP with the momentum in host memory: its device copy
 };
 
 struct LaunchCtx {

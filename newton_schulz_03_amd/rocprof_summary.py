@@ -27,9 +27,9 @@ import sys
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 
-# Sources that determine the matrix-core kernels' memory traffic.
+# Device sources of the matrix-core kernels (their code, and so their memory traffic).
 KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_common.hpp",
-                  "csrc/muon_internal.hpp", "csrc/muon_abi.hip")
+                  "csrc/muon_internal.hpp")
 
 SHORT_NAMES = (("k_gemm_bf16<0>", "gram"), ("k_gemm_bf16<1>", "poly"), ("k_gemm_bf16<2>", "prod"),
                ("k_gemm_staged", "gemm_fp32"), ("k_reduce", "reduce"), ("k_normalize", "normalize"),

@@ -46,7 +46,7 @@ def expected_workspace(shapes, esize):
         return (x + a - 1) // a * a
 
     batch = len(shapes)
-    desc = 112  # sizeof(MatDesc)
+    desc = 128  # sizeof(MatDesc)
     total = up(desc * batch, 256) + up(4 * 5 * (batch + 1), 256)
     total += up(4 * batch, 256)  # per-matrix 1 / (||U|| + eps)
     vec = 16 // esize
@@ -87,8 +87,8 @@ def ns_call(lib, batch=1, rows=(64,), cols=(96,), x=(FAKE,), out=(FAKE + 4096,),
 
 
 def step_call(lib, w=FAKE, g=FAKE + 8192, m=FAKE + 16384, rows=(64,), cols=(96,), nesterov=0,
-              lr=0.02, beta=0.95, ws=FAKE + (1 << 20), ws_bytes=1 << 40, steps=5):
-    p = StepParams(lr, beta, nesterov, NsParams(steps, 3.4445, -4.775, 2.0315, 1e-7))
+              lr=0.02, beta=0.95, ws=FAKE + (1 << 20), ws_bytes=1 << 40, steps=5, mhost=0):
+    p = StepParams(lr, beta, nesterov, NsParams(steps, 3.4445, -4.775, 2.0315, 1e-7), mhost)
     return lib.muon_step_batched(1, _i64_array(rows), _i64_array(cols), _ptr_array([w]),
                                  _ptr_array([g]), _ptr_array([m]), 0, ctypes.byref(p),
                                  ctypes.c_void_p(ws), ws_bytes, None)
@@ -127,6 +127,7 @@ def test_step_validation(lib):
     assert step_call(lib, steps=-2) == E.MUON_ERR_INVALID_ARG
     assert step_call(lib, g=0) == E.MUON_ERR_INVALID_ARG
     assert step_call(lib, ws_bytes=16) == E.MUON_ERR_WORKSPACE
+    assert step_call(lib, mhost=2) == E.MUON_ERR_INVALID_ARG
 
 
 def adamw_call(lib, batch=1, numel=(100,), p=(FAKE,), g=(FAKE + 4096,), m=(FAKE + 8192,),

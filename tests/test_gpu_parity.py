@@ -219,3 +219,44 @@ def test_workspace_reuse_across_shapes():
     torch.cuda.synchronize()
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
     assert torch.equal(b[0].view(torch.int16), c[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,nesterov", [("bf16", False), ("bf16", True), ("fp32", False)])
+def test_step_momentum_in_host_memory(dtype, nesterov):
+    """The momentum kept in pinned host memory gives bit-identical results."""
+    shapes = [(300, 700), (700, 300), (513, 257), (64, 2048)]
+    wl = _wl("muon", dtype, shapes, nesterov=nesterov)
+    ins = device_inputs(wl)
+    w_dev = [d["w"].clone() for d in ins]
+    m_dev = [d["m"].clone() for d in ins]
+    g = [d["g"] for d in ins]
+    w_host = [d["w"].clone() for d in ins]
+    m_host = [d["m"].cpu().pin_memory() for d in ins]
+    nsa.step_batched(w_dev, g, m_dev, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5)
+    nsa.step_batched(w_host, g, m_host, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5,
+                     momentum_host=True)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(w_dev[i], w_host[i]), i
+        assert torch.equal(m_dev[i].cpu(), m_host[i]), i
+    # a second step from the state left in host memory
+    nsa.step_batched(w_dev, g, m_dev, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5)
+    nsa.step_batched(w_host, g, m_host, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5,
+                     momentum_host=True)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(w_dev[i], w_host[i]) and torch.equal(m_dev[i].cpu(), m_host[i]), i
+
+
+def test_momentum_host_rejects_device_memory():
+    wl = _wl("muon", "bf16", [(64, 96)])
+    d = device_inputs(wl)[0]
+    lib = nsa.load_library()
+    from newton_schulz_03_amd._binding import NsParams, StepParams, _i64_array, _ptr_array
+    import ctypes
+    ws = nsa.allocate_workspace([(64, 96)], torch.bfloat16, "cuda")
+    p = StepParams(0.02, 0.95, 0, NsParams(5, 3.4445, -4.775, 2.0315, 1e-7), 1)
+    st = lib.muon_step_batched(1, _i64_array([64]), _i64_array([96]), _ptr_array([d["w"].data_ptr()]),
+                               _ptr_array([d["g"].data_ptr()]), _ptr_array([d["m"].data_ptr()]), 0,
+                               ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+    assert st == nsa.MUON_ERR_INVALID_ARG and "pinned host" in nsa.last_error_detail()
