@@ -260,3 +260,24 @@ def test_momentum_host_rejects_device_memory():
                                _ptr_array([d["g"].data_ptr()]), _ptr_array([d["m"].data_ptr()]), 0,
                                ctypes.byref(p), ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
     assert st == nsa.MUON_ERR_INVALID_ARG and "pinned host" in nsa.last_error_detail()
+
+
+def test_ns_on_second_stream_during_gemm_load_is_unchanged():
+    """The orthogonalization on its own stream, while bf16 products run on another
+    (default priorities), gives the same bits as alone."""
+    wl = _wl("gauss", "bf16", [(512, 1536), (1536, 512), (1024, 1024)])
+    xs = [d["x"] for d in device_inputs(wl)]
+    alone = nsa.ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    a = torch.randn(4096, 6144, device="cuda").to(torch.bfloat16)
+    b = (torch.randn(6144, 2048, device="cuda") * 0.02).to(torch.bfloat16)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(sa):
+        for _ in range(20):
+            torch.matmul(a, b)
+    with torch.cuda.stream(sb):
+        both = nsa.ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    for x, y in zip(alone, both):
+        assert torch.equal(x, y)
