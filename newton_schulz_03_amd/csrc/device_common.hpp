@@ -69,11 +69,16 @@ __device__ __forceinline__ u32x4_t f32_to_vec(const float* in) {
   return v;
 }
 
+// 16-byte loads and stores of global memory.  The pointers come from
+// descriptors and are generic; naming the global address space makes these
+// global_load/global_store instructions, which wait on vmcnt alone (a flat
+// access would also hold lgkmcnt, and so every later wait for an LDS read).
+#define GLOBAL_AS __attribute__((address_space(1)))
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
+  return *(const GLOBAL_AS u32x4_t*)(p);
 }
 __device__ __forceinline__ void st16(void* p, const u32x4_t& v) {
-  *reinterpret_cast<u32x4_t*>(p) = v;
+  *(GLOBAL_AS u32x4_t*)(p) = v;
 }
 
 // Sum over a wavefront of 64 lanes with a fixed butterfly order (deterministic).
