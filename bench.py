@@ -443,7 +443,7 @@ def main(argv=None) -> int:
     achieved = alg_prod_launch / (prod_ms * 1e-3) / 1e12
     per_kernel = {k: {"avg_ms": round(avg(k), 4), "launches": kern[k][1]} for k in nsa.KERNELS
                   if kern[k][1]}
-    ns_ms = (kern["gram"][0] + kern["poly"][0] + kern["prod"][0]) / args.steps
+    ns_ms = (kern["gram"][0] + kern["poly"][0] + kern["prod"][0] + kern["prod_finish"][0]) / args.steps
     ew = [elementwise_bytes(s, esize, wl.call, wl.nesterov) for s in shapes]
     for name, idx in (("reduce", 0), ("normalize", 1), ("finish", 2)):
         if name not in per_kernel:

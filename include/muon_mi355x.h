@@ -193,9 +193,10 @@ typedef enum {
   MUON_K_GRAM = 2,      /* A = X X^T */
   MUON_K_POLY = 3,      /* B = b A + c A^2 */
   MUON_K_PROD = 4,      /* X <- a X + B X */
-  MUON_K_FINISH = 5,    /* W update, or the output copy */
+  MUON_K_FINISH = 5,    /* W update, or the output copy (fp32, or no Newton-Schulz steps) */
   MUON_K_ADAMW = 6,     /* muon_adamw_batched */
-  MUON_K_COUNT = 7
+  MUON_K_PROD_FINISH = 7, /* bf16: the last X <- a X + B X, writing W (or the output) itself */
+  MUON_K_COUNT = 8
 } muon_kernel;
 
 /*

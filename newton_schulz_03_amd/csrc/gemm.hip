@@ -215,18 +215,19 @@ hipError_t launch_mode(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const 
 
 hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
                        float out_scale) {
-  GemmArgs g{cur, 0.f, out_scale, 0};
+  GemmArgs g{cur, 0.f, out_scale, 0, FIN_NONE, 0.f};
   return launch_mode<GM_GRAM>(c, nblocks, is_bf16, g);
 }
 
 hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc) {
-  GemmArgs g{0, b / cc, cc, 0};
+  GemmArgs g{0, b / cc, cc, 0, FIN_NONE, 0.f};
   return launch_mode<GM_POLY>(c, nblocks, is_bf16, g);
 }
 
 hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur, float a,
-                       bool use_poly) {
-  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0};
+                       bool use_poly, int32_t finish, float lr) {
+  if (finish != FIN_NONE && !is_bf16) return hipErrorInvalidValue;  // fp32 keeps the finish kernel
+  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, finish, lr};
   return launch_mode<GM_PROD>(c, nblocks, is_bf16, g);
 }
 

@@ -171,13 +171,11 @@ __device__ __forceinline__ u32x4_t lds_tr(const char* p0, const char* p1) {
 //   GRAM/POLY  T[q][p] = S[tj*256 + q][ti*256 + p] (the mirror); rows go out to
 //              the mirror position, and for ti != tj the columns of T, read with
 //              ds_read_b64_tr_b16, go out as rows of S[ti*256 + p][tj*256 + q].
-template <int MODE>
-__device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], const TileRef& tr,
-                                               const GemmArgs& g, char* smem, int wave,
-                                               int lane) {
+// Accumulator tile -> T in LDS (bf16, scaled), then a barrier.
+__device__ __forceinline__ void stage_tile(const f32x16_t (&acc)[4][4], float scale, char* smem,
+                                           int wave, int lane) {
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
-  const float scale = MODE == GM_PROD ? 1.f : g.out_scale;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -194,6 +192,147 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
         *reinterpret_cast<u32x2_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4) + 8 * lh) = w;
       }
   __syncthreads();
+}
+
+// Eight consecutive q of column p of T (two transposed reads), for the lanes
+// of wave-instruction I: p = 16 (I >> 3) + (lane & 15), q = 8 (4 (I & 7) + lane / 16) + 0..7.
+__device__ __forceinline__ u32x4_t read_tile_column(const char* smem, int I, int lane) {
+  const int pb = I >> 3, cq = 4 * (I & 7) + (lane >> 4);
+  const int r = (lane >> 2) & 3, qq = lane & 3;
+  u32x4_t v;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * cq + 4 * h + r;
+    const int chunk = 2 * pb + (qq >> 1);
+    const char* a = smem + row * MNROW + ((chunk ^ (row & 31)) << 4) + 8 * (qq & 1);
+    const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a));
+    const u32x2_t xu = __builtin_bit_cast(u32x2_t, x);
+    v[2 * h] = xu[0];
+    v[2 * h + 1] = xu[1];
+  }
+  return v;
+}
+
+// Piece u of this thread in the final store: user row (within the tile) and
+// first of 8 user columns, and the 8 elements of T it carries.  A wide matrix
+// takes rows of T, a tall one columns of T (its rows).
+template <bool TALL>
+struct FinalPiece {
+  static __device__ __forceinline__ int row(int u, int wave, int lane) {
+    return TALL ? 16 * ((32 * wave + u) >> 3) + (lane & 15) : (threadIdx.x >> 5) + 8 * u;
+  }
+  static __device__ __forceinline__ int col(int u, int wave, int lane) {
+    return TALL ? 8 * (4 * ((32 * wave + u) & 7) + (lane >> 4)) : 8 * (threadIdx.x & 31);
+  }
+  static __device__ __forceinline__ u32x4_t tile(const char* smem, int u, int wave, int lane) {
+    if constexpr (TALL) {
+      return read_tile_column(smem, 32 * wave + u, lane);
+    } else {
+      const int q = (threadIdx.x >> 5) + 8 * u, c = threadIdx.x & 31;
+      return *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4));
+    }
+  }
+};
+
+// A tile wholly inside the user's matrix, whose rows are whole 16-byte vectors:
+// the W pieces are loaded ahead in two halves, so that their latency hides
+// behind the staging and behind the first half's stores.
+template <bool TALL>
+__device__ __forceinline__ void store_final_interior(const f32x16_t (&acc)[4][4], uint16_t* base,
+                                                     int64_t cols, bool upd, float step,
+                                                     char* smem, int wave, int lane) {
+  using P = FinalPiece<TALL>;
+  u32x4_t w[32];
+  if (upd) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) w[u] = ld16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane));
+  }
+  stage_tile(acc, 1.f, smem, wave, lane);
+  if (upd) {
+#pragma unroll
+    for (int u = 16; u < 32; ++u) w[u] = ld16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane));
+  }
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    u32x4_t v = P::tile(smem, u, wave, lane);
+    if (upd) {
+      float x[8], wf[8];
+      vec_to_f32<uint16_t>(v, x);
+      vec_to_f32<uint16_t>(w[u], wf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = wf[e] - step * x[e];
+      v = f32_to_vec<uint16_t>(x);
+    }
+    st16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane), v);
+  }
+}
+
+// A tile on the matrix's edge: element by element where the 16-byte vector
+// does not fit, every piece clipped to the shape.
+template <bool TALL>
+__device__ __forceinline__ void store_final_edge(const f32x16_t (&acc)[4][4], const MatDesc& d,
+                                                 int64_t ur0, int64_t uc0, bool upd, float step,
+                                                 char* smem, int wave, int lane) {
+  using P = FinalPiece<TALL>;
+  uint16_t* __restrict__ out = static_cast<uint16_t*>(d.dst);
+  const int64_t rows = d.rows, cols = d.cols;
+  stage_tile(acc, 1.f, smem, wave, lane);
+#pragma unroll 1
+  for (int u = 0; u < 32; ++u) {
+    const int64_t r = ur0 + P::row(u, wave, lane), c = uc0 + P::col(u, wave, lane);
+    const u32x4_t xv = P::tile(smem, u, wave, lane);
+    if (r >= rows || c >= cols) continue;
+    float x[8];
+    vec_to_f32<uint16_t>(xv, x);
+    uint16_t* o = out + r * cols + c;
+    if (d.vec_ok && c + 8 <= cols) {
+      if (upd) {
+        float wf[8];
+        vec_to_f32<uint16_t>(ld16(o), wf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = wf[e] - step * x[e];
+      }
+      st16(o, f32_to_vec<uint16_t>(x));
+    } else {
+#pragma unroll 1
+      for (int e = 0; e < 8 && c + e < cols; ++e)
+        o[e] = Elt<uint16_t>::from_f32(upd ? Elt<uint16_t>::to_f32(o[e]) - step * x[e] : x[e]);
+    }
+  }
+}
+
+// The last product of a call: the user's matrix receives W - lr * scale * X'
+// (FIN_STEP) or X' (FIN_NS), in its own orientation and clipped to its shape,
+// and the iterate is not stored.  T[q][p] = X'[ti*256 + q][tj*256 + p] is
+// staged in LDS as for the iterate.
+__device__ __forceinline__ void store_final(const f32x16_t (&acc)[4][4], const TileRef& tr,
+                                            const GemmArgs& g, char* smem, int wave, int lane) {
+  const MatDesc& d = tr.d;
+  const bool tall = d.tall != 0;
+  const bool upd = g.finish == FIN_STEP;
+  const float step = g.lr * d.scale;
+  const int64_t ur0 = static_cast<int64_t>(tall ? tr.tj : tr.ti) * kTile;  // user rows of the tile
+  const int64_t uc0 = static_cast<int64_t>(tall ? tr.ti : tr.tj) * kTile;  // user columns
+  const bool interior = d.vec_ok && ur0 + kTile <= d.rows && uc0 + kTile <= d.cols;
+  uint16_t* base = static_cast<uint16_t*>(d.dst) + ur0 * d.cols + uc0;
+  if (interior) {
+    if (tall)
+      store_final_interior<true>(acc, base, d.cols, upd, step, smem, wave, lane);
+    else
+      store_final_interior<false>(acc, base, d.cols, upd, step, smem, wave, lane);
+  } else {
+    if (tall)
+      store_final_edge<true>(acc, d, ur0, uc0, upd, step, smem, wave, lane);
+    else
+      store_final_edge<false>(acc, d, ur0, uc0, upd, step, smem, wave, lane);
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], const TileRef& tr,
+                                               const GemmArgs& g, char* smem, int wave,
+                                               int lane) {
+  stage_tile(acc, MODE == GM_PROD ? 1.f : g.out_scale, smem, wave, lane);
   const int t = threadIdx.x;
   // Rows of T: thread t moves chunk (t & 31) of rows (t >> 5) + 8u.
   {
@@ -228,23 +367,11 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
       const int64_t r0 = static_cast<int64_t>(tr.ti) * kTile;
       const int64_t c0 = static_cast<int64_t>(tr.tj) * kTile;
       const int grp = lane >> 4, j = lane & 15;
-      const int r = (lane >> 2) & 3, qq = lane & 3;
 #pragma unroll 4
       for (int u = 0; u < 32; ++u) {
         const int I = 32 * wave + u;
         const int pb = I >> 3, cq = 4 * (I & 7) + grp;
-        u32x4_t v;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 8 * cq + 4 * h + r;
-          const int chunk = 2 * pb + (qq >> 1);
-          const char* a = smem + row * MNROW + ((chunk ^ (row & 31)) << 4) + 8 * (qq & 1);
-          const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a));
-          const u32x2_t xu = __builtin_bit_cast(u32x2_t, x);
-          v[2 * h] = xu[0];
-          v[2 * h + 1] = xu[1];
-        }
-        st16(dst + slab_off(r0 + 16 * pb + j, c0 + 8 * cq, ld), v);
+        st16(dst + slab_off(r0 + 16 * pb + j, c0 + 8 * cq, ld), read_tile_column(smem, I, lane));
       }
     }
   }
@@ -457,6 +584,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   }
   wait_vm<0>();  // no load may still target LDS: the ring is reused for the store
   __syncthreads();
+  if constexpr (MODE == GM_PROD) {
+    if (g.finish != FIN_NONE) {
+      store_final(acc, tr, g, smem, wave, lane);
+      return;
+    }
+  }
   store_tile_lds<MODE>(acc, tr, g, smem, wave, lane);
 }
 

@@ -22,11 +22,18 @@ enum GemmMode : int { GM_GRAM = 0, GM_POLY = 1, GM_PROD = 2 };
 //   PROD  acc = Q X + s X,        X' = acc                     (s = a)
 // The s-multiple of the source tile is added inside the K loop by the bf16
 // kernel (matrix cores, see gemm_bf16.hip) and at store time by the fp32 one.
+// The last product of a call can hand its result straight to the user's
+// matrix instead of the workspace (bf16 kernel): FIN_STEP writes
+// W - lr * scale * X', FIN_NS writes X' to the output.
+enum FinishMode : int { FIN_NONE = 0, FIN_STEP = 1, FIN_NS = 2 };
+
 struct GemmArgs {
   int32_t cur;        // X buffer holding the current iterate
   float init_scale;   // POLY: b/c;  PROD: a
   float out_scale;    // GRAM: 1 or b;  POLY: c;  PROD: 1
   int32_t use_poly;   // PROD: Q = B (1) or A (0)
+  int32_t finish;     // PROD: FinishMode
+  float lr;           // PROD with FIN_STEP: learning rate
 };
 
 template <typename T>

@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "gemm_common.hpp"
 #include "muon_internal.hpp"
 #include "muon_mi355x.h"
 
@@ -339,6 +340,8 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
     t.done();
   }
   const bool use_poly = ns.c != 0.f;
+  // bf16: the last product writes the user's matrix itself (no finish pass)
+  const bool fused = pl.bf16 && ns.steps > 0;
   int32_t cur = 0;
   for (int k = 0; k < ns.steps; ++k) {
     {
@@ -354,14 +357,18 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
         return hip_fail(e, "launch polynomial");
       t.done();
     }
+    const bool last = fused && k + 1 == ns.steps;
     {
-      TimedLaunch t(MUON_K_PROD, stream);
-      if ((e = launch_prod(c, pl.totals[PH_PROD], pl.bf16, cur, ns.a, use_poly)) != hipSuccess)
+      TimedLaunch t(last ? MUON_K_PROD_FINISH : MUON_K_PROD, stream);
+      const int32_t fin = !last ? FIN_NONE : ep.mode == MODE_STEP ? FIN_STEP : FIN_NS;
+      if ((e = launch_prod(c, pl.totals[PH_PROD], pl.bf16, cur, ns.a, use_poly, fin, ep.lr)) !=
+          hipSuccess)
         return hip_fail(e, "launch product");
       t.done();
     }
     cur ^= 1;
   }
+  if (fused) return MUON_OK;
   ElemParams fp = ep;
   fp.cur = cur;
   {

@@ -104,7 +104,9 @@ hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_
 // B = b A + c A A  (c != 0)
 hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc);
 // X[next] = a X[cur] + Q X[cur] with Q = B (use_poly) or the already scaled A.
-hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur, float a,
-                       bool use_poly);
+// finish != 0 (bf16 only): the last product of the call, whose result goes to
+// the user's matrix (W - lr * scale * X', or the output) instead of X[next].
+hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
+                       float a, bool use_poly, int32_t finish = 0, float lr = 0.f);
 
 }  // namespace muon
