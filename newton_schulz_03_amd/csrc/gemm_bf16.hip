@@ -379,7 +379,8 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
 
 }  // namespace
 
-template <int MODE>
+// FINAL (products only): the last product of a call, storing with store_final.
+template <int MODE, bool FINAL>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDSB];
 
@@ -584,26 +585,30 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   }
   wait_vm<0>();  // no load may still target LDS: the ring is reused for the store
   __syncthreads();
-  if constexpr (MODE == GM_PROD) {
-    if (g.finish != FIN_NONE) {
-      store_final(acc, tr, g, smem, wave, lane);
-      return;
-    }
-  }
-  store_tile_lds<MODE>(acc, tr, g, smem, wave, lane);
+  if constexpr (FINAL)
+    store_final(acc, tr, g, smem, wave, lane);
+  else
+    store_tile_lds<MODE>(acc, tr, g, smem, wave, lane);
 }
 
 hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, const GemmArgs& g) {
   if (nblocks <= 0) return hipSuccess;
   switch (mode) {
     case GM_GRAM:
-      hipLaunchKernelGGL(k_gemm_bf16<GM_GRAM>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, g);
+      hipLaunchKernelGGL((k_gemm_bf16<GM_GRAM, false>), dim3(nblocks), dim3(kThreads), 0, c.stream,
+                         c, g);
       break;
     case GM_POLY:
-      hipLaunchKernelGGL(k_gemm_bf16<GM_POLY>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, g);
+      hipLaunchKernelGGL((k_gemm_bf16<GM_POLY, false>), dim3(nblocks), dim3(kThreads), 0, c.stream,
+                         c, g);
       break;
     default:
-      hipLaunchKernelGGL(k_gemm_bf16<GM_PROD>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, g);
+      if (g.finish != FIN_NONE)
+        hipLaunchKernelGGL((k_gemm_bf16<GM_PROD, true>), dim3(nblocks), dim3(kThreads), 0,
+                           c.stream, c, g);
+      else
+        hipLaunchKernelGGL((k_gemm_bf16<GM_PROD, false>), dim3(nblocks), dim3(kThreads), 0,
+                           c.stream, c, g);
       break;
   }
   return hipGetLastError();

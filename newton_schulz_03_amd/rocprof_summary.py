@@ -31,9 +31,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_common.hpp",
                   "csrc/muon_internal.hpp")
 
-SHORT_NAMES = (("k_gemm_bf16<0>", "gram"), ("k_gemm_bf16<1>", "poly"), ("k_gemm_bf16<2>", "prod"),
+SHORT_NAMES = (("k_gemm_bf16<0,false>", "gram"), ("k_gemm_bf16<1,false>", "poly"),
+               ("k_gemm_bf16<2,false>", "prod"), ("k_gemm_bf16<2,true>", "prod_finish"),
                ("k_gemm_staged", "gemm_fp32"), ("k_reduce", "reduce"), ("k_normalize", "normalize"),
-               ("k_finish", "finish"), ("k_finalize", "finalize"))
+               ("k_finish", "finish"), ("k_finalize", "finalize"), ("k_adamw", "adamw"))
 
 
 def kernel_source_digest() -> str:
