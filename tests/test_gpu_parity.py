@@ -281,3 +281,51 @@ def test_ns_on_second_stream_during_gemm_load_is_unchanged():
     torch.cuda.synchronize()
     for x, y in zip(alone, both):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_maximum_dimension(dtype):
+    """The longest side the ABI accepts (65536), both orientations, against the oracle."""
+    n = nsa.MAX_DIM
+    _ns_check(dtype, [(3, n), (n, 5)])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_rank_deficient_inputs(dtype):
+    """Rank-1 and rank-deficient matrices.
+
+    Exact zero rows and columns stay exactly zero.  Directions of the null
+    space are not fixed by the input: rounding (the input's to the dtype, and
+    each product's) puts noise there that each step multiplies by up to
+    a = 3.4445, so several outputs are correct in them.  The oracle check is
+    therefore on the input directions with normalized singular value >= 1e-2
+    (to 2e-2 in bf16, 1e-4 in fp32).  In fp32 the whole output is also bounded:
+    1e-7 rounding times a^4 over a few hundred null directions is a few 1e-4,
+    so the full-matrix error must stay below 1e-3.
+    """
+    rng = np.random.default_rng(5)
+    mats = []
+    u = rng.standard_normal((300, 1)); v = rng.standard_normal((1, 700))
+    mats.append(u @ v)                                # rank 1, wide
+    b = rng.standard_normal((520, 40)) @ rng.standard_normal((40, 260))
+    mats.append(b)                                    # rank 40, tall
+    z = rng.standard_normal((257, 513)); z[100:, :] = 0.0
+    mats.append(z)                                    # zero rows
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xs = [torch.from_numpy(m.astype(np.float32)).to(tdt).cuda() for m in mats]
+    outs = nsa.ns_batched(xs, steps=5)
+    torch.cuda.synchronize()
+    for x, o in zip(xs, outs):
+        xh, oh = host_f64(x), host_f64(o)
+        want = oracle.newton_schulz(xh, 5)
+        u, sv, vt = np.linalg.svd(xh, full_matrices=False)
+        keep = sv / np.linalg.norm(sv) >= 1e-2
+        uk, vk = u[:, keep], vt[keep].T
+        ref = uk.T @ want @ vk
+        assert np.linalg.norm(uk.T @ oh @ vk - ref) / np.linalg.norm(ref) <= TOL[dtype]
+        if dtype == "fp32":
+            assert rel_fro(oh, want) <= 1e-3
+        # rows (columns) of the input that are zero stay exactly zero in the output
+        zr = np.all(xh == 0, axis=1)
+        zc = np.all(xh == 0, axis=0)
+        assert np.all(oh[zr, :] == 0) and np.all(oh[:, zc] == 0)
