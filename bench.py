@@ -257,9 +257,10 @@ def bench_overlap(args) -> int:
                 torch.matmul(act, w_up, out=hid)
                 torch.matmul(hid, w_down, out=out)
 
-    def dense(stream):
+    def dense(stream, budget=0):
         with torch.cuda.stream(stream):
-            nsa.ns_batched(X, steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps, out=OUT, workspace=ws)
+            nsa.ns_batched(X, steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps, out=OUT, workspace=ws,
+                           cu_budget=budget)
 
     def timed(fn):
         torch.cuda.synchronize(dev)
@@ -287,6 +288,11 @@ def bench_overlap(args) -> int:
     t_both = min(timed(lambda: (experts(sa), dense(sb))) for _ in range(3))
     t_copy = min(timed(lambda: copies(sa)) for _ in range(3))
     t_copy_dense = min(timed(lambda: (copies(sa), dense(sb))) for _ in range(3))
+    budget = args.overlap_cu_budget
+    timed(lambda: (experts(sa), dense(sb, budget)))
+    t_dense_b = min(timed(lambda: dense(sb, budget)) for _ in range(3))
+    t_both_b = min(timed(lambda: (experts(sa), dense(sb, budget))) for _ in range(3))
+    t_copy_b = min(timed(lambda: (copies(sa), dense(sb, budget))) for _ in range(3))
     ref = [o.clone() for o in OUT]
     dense(sb)
     torch.cuda.synchronize(dev)
@@ -304,7 +310,10 @@ def bench_overlap(args) -> int:
                "sum": round(t_exp + t_dense, 3), "both_two_streams": round(t_both, 3),
                "copies_alone": round(t_copy, 3),
                "copies_and_dense_two_streams": round(t_copy_dense, 3),
-               "saved_against_copies": round(t_copy + t_dense - t_copy_dense, 3)},
+               "saved_against_copies": round(t_copy + t_dense - t_copy_dense, 3),
+               f"dense_alone_cu_budget_{budget}": round(t_dense_b, 3),
+               f"experts_and_dense_cu_budget_{budget}": round(t_both_b, 3),
+               f"copies_and_dense_cu_budget_{budget}": round(t_copy_b, 3)},
         "copy_load": f"{args.overlap_copies} x 1 GiB device-to-device copies",
         "dense_output_identical_under_overlap": same,
     }
@@ -343,6 +352,8 @@ def main(argv=None) -> int:
                     help="measure the dense-matrix orthogonalization overlapped with expert GEMMs")
     ap.add_argument("--overlap-gemms", type=int, default=120,
                     help="expert FFN product pairs in the overlap load")
+    ap.add_argument("--overlap-cu-budget", type=int, default=64,
+                    help="CUs the dense orthogonalization keeps in the budgeted overlap runs")
     ap.add_argument("--overlap-copies", type=int, default=100,
                     help="1 GiB device copies in the bandwidth-bound overlap load")
     ap.add_argument("--momentum-host", action="store_true",

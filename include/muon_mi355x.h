@@ -81,6 +81,13 @@ typedef struct {
   int32_t steps;
   float a, b, c;
   float eps;
+  /* 0: the matrix-core launches fill the GPU.  N > 0: each of them (bf16) keeps
+   * at most N workgroups resident, one per CU, each looping over tiles, so that
+   * work on other streams keeps the remaining CUs; this is for orthogonalizing
+   * the dense matrices while expert compute goes on ("How PyTorch Scaled a
+   * Near-1T MoE on Europe's Public Supercomputer", §Three optimizations that
+   * changed the economics, FlexShard bullet).  Results do not depend on it. */
+  int32_t cu_budget;
 } muon_ns_params;
 
 /*

@@ -39,7 +39,7 @@ class MuonError(RuntimeError):
 
 class NsParams(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
-                ("c", ctypes.c_float), ("eps", ctypes.c_float)]
+                ("c", ctypes.c_float), ("eps", ctypes.c_float), ("cu_budget", ctypes.c_int32)]
 
 
 class StepParams(ctypes.Structure):
@@ -170,11 +170,12 @@ def _check_tensors(ts, name):
 
 
 def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
-               out: Optional[Sequence] = None, workspace=None) -> List:
+               out: Optional[Sequence] = None, workspace=None, cu_budget: int = 0) -> List:
     """Newton-Schulz orthogonalization of a ragged batch of matrices on the GPU.
 
     Returns the outputs (new tensors, or `out` when given; out[i] may be xs[i]).
-    Runs on the current HIP stream of the tensors' device.
+    Runs on the current HIP stream of the tensors' device.  cu_budget > 0 keeps
+    the matrix-core launches to that many CUs (the rest stay free for other streams).
     """
     import torch
 
@@ -196,7 +197,7 @@ def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
     if workspace is None:
         workspace = allocate_workspace(shapes, xs[0].dtype, dev)
     a, b, c = (float(v) for v in coeffs)
-    p = NsParams(int(steps), a, b, c, float(eps))
+    p = NsParams(int(steps), a, b, c, float(eps), int(cu_budget))
     with torch.cuda.device(dev):
         st = lib.muon_ns_batched(len(xs), _i64_array([s[0] for s in shapes]),
                                  _i64_array([s[1] for s in shapes]),
@@ -210,7 +211,7 @@ def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
 
 def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, beta: float = 0.95,
                  nesterov: bool = False, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
-                 workspace=None, momentum_host: bool = False) -> None:
+                 workspace=None, momentum_host: bool = False, cu_budget: int = 0) -> None:
     """One Muon step over a ragged batch, in place on ws (weights) and ms (momentum).
 
     momentum_host: the momenta are pinned host tensors (pin_memory), which the
@@ -241,7 +242,8 @@ def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, bet
         workspace = allocate_workspace(shapes, ws[0].dtype, dev)
     a, b, c = (float(v) for v in coeffs)
     p = StepParams(float(lr), float(beta), 1 if nesterov else 0,
-                   NsParams(int(steps), a, b, c, float(eps)), 1 if momentum_host else 0)
+                   NsParams(int(steps), a, b, c, float(eps), int(cu_budget)),
+                   1 if momentum_host else 0)
     with torch.cuda.device(dev):
         st = lib.muon_step_batched(len(ws), _i64_array([s[0] for s in shapes]),
                                    _i64_array([s[1] for s in shapes]),

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
   constexpr int BK = kRowBytes / sizeof(T);
 
   __shared__ int slot;
-  const TileRef tr = decode_tile<MODE>(c, &slot);
+  const TileRef tr = decode_tile<MODE>(c, static_cast<int32_t>(blockIdx.x), g.ntiles, &slot);
   const MatDesc& d = tr.d;
   const int32_t ti = tr.ti, tj = tr.tj;
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
@@ -202,11 +202,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
 
 namespace {
 
+// ntiles tiles; bf16 launches keep at most c.max_blocks workgroups (0: one per tile).
 template <int MODE>
-hipError_t launch_mode(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const GemmArgs& g) {
-  if (nblocks <= 0) return hipSuccess;
-  if (is_bf16) return launch_gemm_bf16(MODE, c, nblocks, g);
-  hipLaunchKernelGGL((k_gemm_staged<float, MODE>), dim3(nblocks), dim3(kThreads), 0, c.stream, c,
+hipError_t launch_mode(const LaunchCtx& c, int32_t ntiles, bool is_bf16, GemmArgs g) {
+  if (ntiles <= 0) return hipSuccess;
+  g.ntiles = ntiles;
+  if (is_bf16) {
+    const int32_t grid = c.max_blocks > 0 && c.max_blocks < ntiles ? c.max_blocks : ntiles;
+    return launch_gemm_bf16(MODE, c, grid, g);
+  }
+  hipLaunchKernelGGL((k_gemm_staged<float, MODE>), dim3(ntiles), dim3(kThreads), 0, c.stream, c,
                      g);
   return hipGetLastError();
 }
@@ -215,19 +220,19 @@ hipError_t launch_mode(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const 
 
 hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
                        float out_scale) {
-  GemmArgs g{cur, 0.f, out_scale, 0, FIN_NONE, 0.f};
+  GemmArgs g{cur, 0.f, out_scale, 0, FIN_NONE, 0.f, 0};
   return launch_mode<GM_GRAM>(c, nblocks, is_bf16, g);
 }
 
 hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc) {
-  GemmArgs g{0, b / cc, cc, 0, FIN_NONE, 0.f};
+  GemmArgs g{0, b / cc, cc, 0, FIN_NONE, 0.f, 0};
   return launch_mode<GM_POLY>(c, nblocks, is_bf16, g);
 }
 
 hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur, float a,
                        bool use_poly, int32_t finish, float lr) {
   if (finish != FIN_NONE && !is_bf16) return hipErrorInvalidValue;  // fp32 keeps the finish kernel
-  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, finish, lr};
+  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, finish, lr, 0};
   return launch_mode<GM_PROD>(c, nblocks, is_bf16, g);
 }
 

@@ -379,13 +379,12 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
 
 }  // namespace
 
-// FINAL (products only): the last product of a call, storing with store_final.
+// One output tile (virtual block v).  FINAL (products only): the last product
+// of a call, storing with store_final.
 template <int MODE, bool FINAL>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDSB];
-
-  __shared__ int slot;
-  const TileRef tr = decode_tile<MODE>(c, &slot);
+__device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g, int32_t v,
+                                          char* smem, int* slot) {
+  const TileRef tr = decode_tile<MODE>(c, v, g.ntiles, slot);
   const MatDesc& d = tr.d;
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
   const uint16_t* Xc = static_cast<const uint16_t*>(iterate(d, g.cur));
@@ -591,24 +590,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
     store_tile_lds<MODE>(acc, tr, g, smem, wave, lane);
 }
 
+// One block per CU, one tile per block.  LOOP (a CU budget: a grid smaller
+// than the tile count): a block takes tiles blockIdx.x, blockIdx.x + gridDim.x,
+// ..., the same order in which a full grid's blocks are dealt out, XCD by XCD.
+// The loop is a separate instantiation: across tiles the compiler keeps
+// tile-invariant values in registers, which the single-tile kernel cannot spare.
+template <int MODE, bool FINAL, bool LOOP>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDSB];
+  __shared__ int slot;
+  if constexpr (LOOP) {
+    for (int32_t v = blockIdx.x; v < g.ntiles; v += gridDim.x) {
+      gemm_tile<MODE, FINAL>(c, g, v, smem, &slot);
+      __syncthreads();  // every wave is done with LDS before the next tile's loads land there
+    }
+  } else {
+    gemm_tile<MODE, FINAL>(c, g, static_cast<int32_t>(blockIdx.x), smem, &slot);
+  }
+}
+
+template <int MODE, bool FINAL>
+void launch_one(const LaunchCtx& c, int32_t nblocks, const GemmArgs& g) {
+  if (nblocks < g.ntiles)
+    hipLaunchKernelGGL((k_gemm_bf16<MODE, FINAL, true>), dim3(nblocks), dim3(kThreads), 0,
+                       c.stream, c, g);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16<MODE, FINAL, false>), dim3(nblocks), dim3(kThreads), 0,
+                       c.stream, c, g);
+}
+
+// nblocks workgroups (at most g.ntiles; fewer under a CU budget).
 hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, const GemmArgs& g) {
   if (nblocks <= 0) return hipSuccess;
   switch (mode) {
-    case GM_GRAM:
-      hipLaunchKernelGGL((k_gemm_bf16<GM_GRAM, false>), dim3(nblocks), dim3(kThreads), 0, c.stream,
-                         c, g);
-      break;
-    case GM_POLY:
-      hipLaunchKernelGGL((k_gemm_bf16<GM_POLY, false>), dim3(nblocks), dim3(kThreads), 0, c.stream,
-                         c, g);
-      break;
+    case GM_GRAM: launch_one<GM_GRAM, false>(c, nblocks, g); break;
+    case GM_POLY: launch_one<GM_POLY, false>(c, nblocks, g); break;
     default:
       if (g.finish != FIN_NONE)
-        hipLaunchKernelGGL((k_gemm_bf16<GM_PROD, true>), dim3(nblocks), dim3(kThreads), 0,
-                           c.stream, c, g);
+        launch_one<GM_PROD, true>(c, nblocks, g);
       else
-        hipLaunchKernelGGL((k_gemm_bf16<GM_PROD, false>), dim3(nblocks), dim3(kThreads), 0,
-                           c.stream, c, g);
+        launch_one<GM_PROD, false>(c, nblocks, g);
       break;
   }
   return hipGetLastError();

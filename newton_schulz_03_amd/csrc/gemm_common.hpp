@@ -34,6 +34,7 @@ struct GemmArgs {
   int32_t use_poly;   // PROD: Q = B (1) or A (0)
   int32_t finish;     // PROD: FinishMode
   float lr;           // PROD with FIN_STEP: learning rate
+  int32_t ntiles;     // tiles of the launch; a block takes tiles blockIdx.x + k * gridDim.x
 };
 
 template <typename T>
@@ -84,12 +85,14 @@ struct TileRef {
   int32_t ti, tj;
 };
 
-// Block -> (matrix, tile) for the symmetric phases (GRAM, POLY) or the product,
-// with blocks renumbered XCD by XCD.  Called by the whole block: the matrix is
+// Virtual block -> (matrix, tile) for the symmetric phases (GRAM, POLY) or the
+// product, with blocks renumbered XCD by XCD.  Called by the whole block: the matrix is
 // located cooperatively, through `slot` in LDS.
 template <int MODE>
-__device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int* slot) {
-  const int32_t b = xcd_remap(static_cast<int32_t>(blockIdx.x), static_cast<int32_t>(gridDim.x));
+__device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int32_t v, int32_t ntiles,
+                                               int* slot) {
+  // virtual block v runs on XCD v % 8 whenever the grid is a multiple of 8
+  const int32_t b = xcd_remap(v, ntiles);
   const int32_t* pre = c.prefix + (MODE == GM_PROD ? PH_PROD : PH_SYM) * (c.batch + 1);
   const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;

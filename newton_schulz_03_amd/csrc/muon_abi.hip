@@ -300,6 +300,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int32_t check_ns_params(const muon_ns_params* p) {
   if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "params pointer is null");
   if (p->steps < 0) return fail(MUON_ERR_INVALID_ARG, "steps = %d is negative", p->steps);
+  if (p->cu_budget < 0)
+    return fail(MUON_ERR_INVALID_ARG, "cu_budget = %d is negative", p->cu_budget);
   if (!std::isfinite(p->a) || !std::isfinite(p->b) || !std::isfinite(p->c) ||
       !std::isfinite(p->eps) || p->eps < 0.f)
     return fail(MUON_ERR_INVALID_ARG, "Newton-Schulz coefficients must be finite and eps >= 0");
@@ -324,6 +326,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   c.partials = reinterpret_cast<float*>(ws + pl.partials_off);
   c.inv_norm = reinterpret_cast<float*>(ws + pl.inv_off);
   c.batch = pl.batch;
+  c.max_blocks = ns.cu_budget;
   c.stream = stream;
   hipError_t e;
   {

@@ -51,6 +51,7 @@ struct LaunchCtx {
   float* partials;         // device: per reduce-block sums of squares
   float* inv_norm;         // device: per matrix 1 / (||U||_F + eps)
   int32_t batch;
+  int32_t max_blocks;      // matrix-core launches: most workgroups resident (0: one per tile)
   hipStream_t stream;
 };
 

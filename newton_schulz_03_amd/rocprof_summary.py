@@ -31,8 +31,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_common.hpp",
                   "csrc/muon_internal.hpp")
 
-SHORT_NAMES = (("k_gemm_bf16<0,false>", "gram"), ("k_gemm_bf16<1,false>", "poly"),
-               ("k_gemm_bf16<2,false>", "prod"), ("k_gemm_bf16<2,true>", "prod_finish"),
+SHORT_NAMES = (("k_gemm_bf16<0,false,false>", "gram"), ("k_gemm_bf16<1,false,false>", "poly"),
+               ("k_gemm_bf16<2,false,false>", "prod"), ("k_gemm_bf16<2,true,false>", "prod_finish"),
+               ("k_gemm_bf16<0,false,true>", "gram_budget"), ("k_gemm_bf16<1,false,true>", "poly_budget"),
+               ("k_gemm_bf16<2,false,true>", "prod_budget"),
+               ("k_gemm_bf16<2,true,true>", "prod_finish_budget"),
                ("k_gemm_staged", "gemm_fp32"), ("k_reduce", "reduce"), ("k_normalize", "normalize"),
                ("k_finish", "finish"), ("k_finalize", "finalize"), ("k_adamw", "adamw"))
 

@@ -76,8 +76,8 @@ def test_workspace_bytes_invalid(lib):
 
 def ns_call(lib, batch=1, rows=(64,), cols=(96,), x=(FAKE,), out=(FAKE + 4096,), dtype=0,
             steps=5, coeffs=(3.4445, -4.775, 2.0315), eps=1e-7, ws=FAKE + (1 << 20),
-            ws_bytes=1 << 40, params=True):
-    p = NsParams(steps, *coeffs, eps)
+            ws_bytes=1 << 40, params=True, budget=0):
+    p = NsParams(steps, *coeffs, eps, budget)
     return lib.muon_ns_batched(batch, _i64_array(rows) if rows is not None else None,
                                _i64_array(cols) if cols is not None else None,
                                _ptr_array(x) if x is not None else None,
@@ -107,6 +107,7 @@ def test_ns_validation(lib):
     assert ns_call(lib, params=False) == E.MUON_ERR_INVALID_ARG
     assert ns_call(lib, coeffs=(float("nan"), 0.0, 0.0)) == E.MUON_ERR_INVALID_ARG
     assert ns_call(lib, eps=-1.0) == E.MUON_ERR_INVALID_ARG
+    assert ns_call(lib, budget=-1) == E.MUON_ERR_INVALID_ARG
     assert ns_call(lib, x=None) == E.MUON_ERR_INVALID_ARG
     assert ns_call(lib, x=(0,)) == E.MUON_ERR_INVALID_ARG
     assert ns_call(lib, out=(FAKE + 2,)) == E.MUON_ERR_INVALID_ARG

@@ -329,3 +329,25 @@ def test_rank_deficient_inputs(dtype):
         zr = np.all(xh == 0, axis=1)
         zc = np.all(xh == 0, axis=0)
         assert np.all(oh[zr, :] == 0) and np.all(oh[:, zc] == 0)
+
+
+@pytest.mark.parametrize("budget", [8, 24, 100])
+def test_cu_budget_gives_identical_results(budget):
+    """A CU budget (fewer workgroups, each looping over tiles) changes only where
+    tiles run: the bits are the same, for the orthogonalization and the step."""
+    shapes = [(300, 700), (700, 300), (1024, 1536), (513, 257)]
+    wl = _wl("muon", "bf16", shapes)
+    ins = device_inputs(wl)
+    g = [d["g"] for d in ins]
+    full = nsa.ns_batched(g, steps=5)
+    some = nsa.ns_batched(g, steps=5, cu_budget=budget)
+    w0 = [d["w"].clone() for d in ins]
+    m0 = [d["m"].clone() for d in ins]
+    w1 = [d["w"].clone() for d in ins]
+    m1 = [d["m"].clone() for d in ins]
+    nsa.step_batched(w0, g, m0, steps=5)
+    nsa.step_batched(w1, g, m1, steps=5, cu_budget=budget)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(full[i], some[i]), i
+        assert torch.equal(w0[i], w1[i]) and torch.equal(m0[i], m1[i]), i
