@@ -27,8 +27,12 @@
  *  - Matrices are dense, row-major, contiguous: element (i, j) of a rows x cols
  *    matrix is at ptr[i*cols + j].  One dtype covers every tensor of a call.
  *  - Device pointers (x, out, w, g, m, workspace) must be 16-byte aligned
- *    device memory of the current HIP device.  Host arrays (rows, cols, the
- *    pointer arrays, the parameter structs) are read during the call only.
+ *    device memory of the current HIP device (m may be pinned host memory, see
+ *    momentum_host).  Host arrays (rows, cols, the pointer arrays, the
+ *    parameter structs) are read during the call only.
+ *  - The buffers of different matrices of one call must not overlap (this is
+ *    not checked); the aliasing allowed within one matrix is stated per entry
+ *    point.
  *  - The caller owns every buffer, the workspace included.  The library
  *    allocates no device memory and keeps no pointer after it returns; it owns
  *    only a small ring of pinned host staging buffers for the descriptor
