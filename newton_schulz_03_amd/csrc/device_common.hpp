@@ -141,9 +141,9 @@ __device__ __forceinline__ int64_t slab_off(int64_t r, int64_t c, int64_t ncols)
 
 // Workgroups are dealt round-robin to the 8 XCDs of the chip (block b runs on
 // XCD b % 8).  Renumber them so that each XCD receives one contiguous range of
-// logical blocks: neighbouring tiles, which share operands, then share an L2.
+// logical blocks, of equal length: neighbouring tiles, which share operands,
+// then share an L2.
 __device__ __forceinline__ int32_t xcd_remap(int32_t b, int32_t n) {
-  constexpr int kXcd = 8;
   const int32_t xcd = b % kXcd, local = b / kXcd;
   const int32_t per = n / kXcd, rem = n % kXcd;
   return xcd * per + (xcd < rem ? xcd : rem) + local;

@@ -123,7 +123,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
   constexpr int BK = kRowBytes / sizeof(T);
 
   __shared__ int slot;
-  const TileRef tr = decode_tile<MODE>(c, static_cast<int32_t>(blockIdx.x), g.ntiles, &slot);
+  const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
+  if (t < 0) return;  // the whole block: t depends on blockIdx.x only
+  const TileRef tr = decode_tile<MODE>(c, t, &slot);
   const MatDesc& d = tr.d;
   const int32_t ti = tr.ti, tj = tr.tj;
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
@@ -202,38 +204,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
 
 namespace {
 
-// ntiles tiles; bf16 launches keep at most c.max_blocks workgroups (0: one per tile).
+// The tiles that sp splits.  bf16 launches under a CU budget (c.max_blocks
+// workgroups, fewer than one per tile) loop over the tiles instead.
 template <int MODE>
-hipError_t launch_mode(const LaunchCtx& c, int32_t ntiles, bool is_bf16, GemmArgs g) {
+hipError_t launch_mode(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, GemmArgs g) {
+  const int32_t ntiles = sp.lo[kXcd];
   if (ntiles <= 0) return hipSuccess;
   g.ntiles = ntiles;
+  g.split = sp;
   if (is_bf16) {
-    const int32_t grid = c.max_blocks > 0 && c.max_blocks < ntiles ? c.max_blocks : ntiles;
-    return launch_gemm_bf16(MODE, c, grid, g);
+    const bool loop = c.max_blocks > 0 && c.max_blocks < sp.grid;
+    const int32_t grid = !loop ? sp.grid : c.max_blocks < ntiles ? c.max_blocks : ntiles;
+    return launch_gemm_bf16(MODE, c, grid, loop, g);
   }
-  hipLaunchKernelGGL((k_gemm_staged<float, MODE>), dim3(ntiles), dim3(kThreads), 0, c.stream, c,
+  hipLaunchKernelGGL((k_gemm_staged<float, MODE>), dim3(sp.grid), dim3(kThreads), 0, c.stream, c,
                      g);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
+hipError_t launch_gram(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur,
                        float out_scale) {
-  GemmArgs g{cur, 0.f, out_scale, 0, FIN_NONE, 0.f, 0};
-  return launch_mode<GM_GRAM>(c, nblocks, is_bf16, g);
+  GemmArgs g{cur, 0.f, out_scale, 0, FIN_NONE, 0.f, 0, {}};
+  return launch_mode<GM_GRAM>(c, sp, is_bf16, g);
 }
 
-hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc) {
-  GemmArgs g{0, b / cc, cc, 0, FIN_NONE, 0.f, 0};
-  return launch_mode<GM_POLY>(c, nblocks, is_bf16, g);
+hipError_t launch_poly(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, float b, float cc) {
+  GemmArgs g{0, b / cc, cc, 0, FIN_NONE, 0.f, 0, {}};
+  return launch_mode<GM_POLY>(c, sp, is_bf16, g);
 }
 
-hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur, float a,
+hipError_t launch_prod(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur, float a,
                        bool use_poly, int32_t finish, float lr) {
   if (finish != FIN_NONE && !is_bf16) return hipErrorInvalidValue;  // fp32 keeps the finish kernel
-  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, finish, lr, 0};
-  return launch_mode<GM_PROD>(c, nblocks, is_bf16, g);
+  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, finish, lr, 0, {}};
+  return launch_mode<GM_PROD>(c, sp, is_bf16, g);
 }
 
 }  // namespace muon

@@ -379,12 +379,12 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
 
 }  // namespace
 
-// One output tile (virtual block v).  FINAL (products only): the last product
+// One output tile (tile number t of the launch).  FINAL (products only): the last product
 // of a call, storing with store_final.
 template <int MODE, bool FINAL>
-__device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g, int32_t v,
+__device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g, int32_t t,
                                           char* smem, int* slot) {
-  const TileRef tr = decode_tile<MODE>(c, v, g.ntiles, slot);
+  const TileRef tr = decode_tile<MODE>(c, t, slot);
   const MatDesc& d = tr.d;
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
   const uint16_t* Xc = static_cast<const uint16_t*>(iterate(d, g.cur));
@@ -590,28 +590,31 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
     store_tile_lds<MODE>(acc, tr, g, smem, wave, lane);
 }
 
-// One block per CU, one tile per block.  LOOP (a CU budget: a grid smaller
-// than the tile count): a block takes tiles blockIdx.x, blockIdx.x + gridDim.x,
-// ..., the same order in which a full grid's blocks are dealt out, XCD by XCD.
-// The loop is a separate instantiation: across tiles the compiler keeps
-// tile-invariant values in registers, which the single-tile kernel cannot spare.
+// One block per CU, one tile per block, taken by split_tile: the XCDs get
+// ranges of equal work.  LOOP (a CU budget: fewer workgroups than tiles): a
+// block takes tiles blockIdx.x, blockIdx.x + gridDim.x, ..., renumbered so that
+// each XCD walks one contiguous range of equal length.  The loop is a separate
+// instantiation: across tiles the compiler keeps tile-invariant values in
+// registers, which the single-tile kernel cannot spare.
 template <int MODE, bool FINAL, bool LOOP>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDSB];
   __shared__ int slot;
   if constexpr (LOOP) {
     for (int32_t v = blockIdx.x; v < g.ntiles; v += gridDim.x) {
-      gemm_tile<MODE, FINAL>(c, g, v, smem, &slot);
+      gemm_tile<MODE, FINAL>(c, g, xcd_remap(v, g.ntiles), smem, &slot);
       __syncthreads();  // every wave is done with LDS before the next tile's loads land there
     }
   } else {
-    gemm_tile<MODE, FINAL>(c, g, static_cast<int32_t>(blockIdx.x), smem, &slot);
+    const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
+    if (t < 0) return;  // the whole block: t depends on blockIdx.x only
+    gemm_tile<MODE, FINAL>(c, g, t, smem, &slot);
   }
 }
 
 template <int MODE, bool FINAL>
-void launch_one(const LaunchCtx& c, int32_t nblocks, const GemmArgs& g) {
-  if (nblocks < g.ntiles)
+void launch_one(const LaunchCtx& c, int32_t nblocks, bool loop, const GemmArgs& g) {
+  if (loop)
     hipLaunchKernelGGL((k_gemm_bf16<MODE, FINAL, true>), dim3(nblocks), dim3(kThreads), 0,
                        c.stream, c, g);
   else
@@ -619,17 +622,19 @@ void launch_one(const LaunchCtx& c, int32_t nblocks, const GemmArgs& g) {
                        c.stream, c, g);
 }
 
-// nblocks workgroups (at most g.ntiles; fewer under a CU budget).
-hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, const GemmArgs& g) {
+// g.split.grid workgroups of one tile each or, with loop, nblocks workgroups
+// (fewer than g.ntiles) looping over the tiles.
+hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, bool loop,
+                            const GemmArgs& g) {
   if (nblocks <= 0) return hipSuccess;
   switch (mode) {
-    case GM_GRAM: launch_one<GM_GRAM, false>(c, nblocks, g); break;
-    case GM_POLY: launch_one<GM_POLY, false>(c, nblocks, g); break;
+    case GM_GRAM: launch_one<GM_GRAM, false>(c, nblocks, loop, g); break;
+    case GM_POLY: launch_one<GM_POLY, false>(c, nblocks, loop, g); break;
     default:
       if (g.finish != FIN_NONE)
-        launch_one<GM_PROD, true>(c, nblocks, g);
+        launch_one<GM_PROD, true>(c, nblocks, loop, g);
       else
-        launch_one<GM_PROD, false>(c, nblocks, g);
+        launch_one<GM_PROD, false>(c, nblocks, loop, g);
       break;
   }
   return hipGetLastError();

@@ -34,7 +34,8 @@ struct GemmArgs {
   int32_t use_poly;   // PROD: Q = B (1) or A (0)
   int32_t finish;     // PROD: FinishMode
   float lr;           // PROD with FIN_STEP: learning rate
-  int32_t ntiles;     // tiles of the launch; a block takes tiles blockIdx.x + k * gridDim.x
+  int32_t ntiles;     // tiles of the launch
+  XcdSplit split;     // one tile per workgroup: which tile workgroup b takes (split_tile)
 };
 
 template <typename T>
@@ -85,14 +86,27 @@ struct TileRef {
   int32_t ti, tj;
 };
 
-// Virtual block -> (matrix, tile) for the symmetric phases (GRAM, POLY) or the
-// product, with blocks renumbered XCD by XCD.  Called by the whole block: the matrix is
-// located cooperatively, through `slot` in LDS.
+// Tile of workgroup b in a launch of one tile per workgroup: b runs on XCD
+// x = b % 8 and takes the (b / 8)-th tile of that XCD's range; -1 past its end
+// (the grid covers the longest range, so shorter ones leave workgroups idle).
+__host__ __device__ __forceinline__ int32_t split_tile(const XcdSplit& s, int32_t b) {
+  const int32_t x = b % kXcd, k = b / kXcd;
+  int32_t lo = s.lo[0], hi = s.lo[1];
+#pragma unroll
+  for (int i = 1; i < kXcd; ++i) {
+    if (x == i) {
+      lo = s.lo[i];
+      hi = s.lo[i + 1];
+    }
+  }
+  return lo + k < hi ? lo + k : -1;
+}
+
+// Tile number b of the launch -> (matrix, tile) for the symmetric phases (GRAM,
+// POLY) or the product.  Called by the whole block: the matrix is located
+// cooperatively, through `slot` in LDS.
 template <int MODE>
-__device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int32_t v, int32_t ntiles,
-                                               int* slot) {
-  // virtual block v runs on XCD v % 8 whenever the grid is a multiple of 8
-  const int32_t b = xcd_remap(v, ntiles);
+__device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int32_t b, int* slot) {
   const int32_t* pre = c.prefix + (MODE == GM_PROD ? PH_PROD : PH_SYM) * (c.batch + 1);
   const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;
@@ -208,7 +222,10 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
   }
 }
 
-// Launches of the bf16 pipelined kernels (gemm_bf16.hip).
-hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, const GemmArgs& g);
+// Launches of the bf16 pipelined kernels (gemm_bf16.hip): g.split.grid
+// workgroups of one tile each, or (loop) nblocks < g.ntiles workgroups that
+// loop over the tiles.
+hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, bool loop,
+                            const GemmArgs& g);
 
 }  // namespace muon

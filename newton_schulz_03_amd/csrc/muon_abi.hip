@@ -42,11 +42,47 @@ struct Plan {
   std::vector<size_t> mat_off;      // byte offset of matrix i's buffers
   std::vector<int32_t> prefix;      // NPHASE x (batch + 1)
   int32_t totals[NPHASE] = {0, 0, 0, 0, 0};
+  XcdSplit split_gram{}, split_poly{}, split_prod{};  // matrix-core launches over the XCDs
   size_t table_bytes = 0;
   size_t inv_off = 0;
   size_t partials_off = 0;
   size_t total_bytes = 0;
 };
+
+// A matrix-core tile costs its 32-wide K slices (about 1350 cycles each) plus
+// a fixed start and store of about 14k cycles, i.e. about 12 slices more.
+constexpr int64_t kTileOverheadSlices = 12;
+
+// Cut the tiles of one matrix-core launch into kXcd contiguous ranges of about
+// equal work: XCD x starts at the first tile with at least x/8 of the launch's
+// work before it.  Matrix i contributes cnt[i] tiles of slices[i] K slices.
+int32_t make_split(const std::vector<int64_t>& cnt, const std::vector<int64_t>& slices,
+                   XcdSplit& sp) {
+  int64_t total = 0;
+  for (size_t i = 0; i < cnt.size(); ++i) total += cnt[i] * (slices[i] + kTileOverheadSlices);
+  int64_t tiles_before = 0, work_before = 0;
+  int x = 1;
+  sp.lo[0] = 0;
+  for (size_t i = 0; i < cnt.size(); ++i) {
+    const int64_t w = slices[i] + kTileOverheadSlices;
+    while (x < kXcd) {
+      // the first tile k of this matrix with 8 * (work_before + k * w) >= x * total
+      const int64_t need = x * total - kXcd * work_before;
+      const int64_t k = need <= 0 ? 0 : cdiv(need, kXcd * w);
+      if (k >= cnt[i]) break;
+      sp.lo[x++] = static_cast<int32_t>(tiles_before + k);
+    }
+    tiles_before += cnt[i];
+    work_before += cnt[i] * w;
+  }
+  while (x <= kXcd) sp.lo[x++] = static_cast<int32_t>(tiles_before);
+  int64_t longest = 0;
+  for (x = 0; x < kXcd; ++x) longest = std::max<int64_t>(longest, sp.lo[x + 1] - sp.lo[x]);
+  if (longest * kXcd > 0x7fffffffLL)
+    return fail(MUON_ERR_UNSUPPORTED, "batch too large: more than 2^31 blocks in one launch");
+  sp.grid = static_cast<int32_t>(longest * kXcd);
+  return MUON_OK;
+}
 
 // Shapes and counts only; no pointers.  Returns MUON_OK or an error (with detail).
 int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype, Plan& pl) {
@@ -64,6 +100,9 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
   pl.mat_off.assign(batch, 0);
   pl.prefix.assign(static_cast<size_t>(NPHASE) * (batch + 1), 0);
   int64_t tot[NPHASE] = {0, 0, 0, 0, 0};
+  // per matrix: symmetric and product tiles; K slices of the Gram (long side)
+  // and of A^2 and the product (short side)
+  std::vector<int64_t> sym_cnt(batch), prod_cnt(batch), k_long(batch), k_short(batch);
   for (int32_t i = 0; i < batch; ++i) {
     const int64_t r = rows[i], c = cols[i];
     if (r <= 0 || c <= 0)
@@ -91,6 +130,10 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
         ts * tl,                                                       // PH_PROD
         cdiv(r, kEwTile) * cdiv(c, kEwTile),                           // PH_FINISH
     };
+    sym_cnt[i] = cnt[PH_SYM];
+    prod_cnt[i] = cnt[PH_PROD];
+    k_long[i] = d.l_pad / 32;
+    k_short[i] = d.s_pad / 32;
     for (int ph = 0; ph < NPHASE; ++ph) {
       pl.prefix[static_cast<size_t>(ph) * (batch + 1) + i] = static_cast<int32_t>(tot[ph]);
       tot[ph] += cnt[ph];
@@ -102,6 +145,10 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
     pl.prefix[static_cast<size_t>(ph) * (batch + 1) + batch] = static_cast<int32_t>(tot[ph]);
     pl.totals[ph] = static_cast<int32_t>(tot[ph]);
   }
+  int32_t st;
+  if ((st = make_split(sym_cnt, k_long, pl.split_gram)) != MUON_OK) return st;
+  if ((st = make_split(sym_cnt, k_short, pl.split_poly)) != MUON_OK) return st;
+  if ((st = make_split(prod_cnt, k_short, pl.split_prod)) != MUON_OK) return st;
   size_t off = 0;
   off += align_up(sizeof(MatDesc) * batch, kAlign);
   off += align_up(sizeof(int32_t) * pl.prefix.size(), kAlign);
@@ -349,14 +396,14 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   for (int k = 0; k < ns.steps; ++k) {
     {
       TimedLaunch t(MUON_K_GRAM, stream);
-      if ((e = launch_gram(c, pl.totals[PH_SYM], pl.bf16, cur, use_poly ? 1.f : ns.b)) !=
+      if ((e = launch_gram(c, pl.split_gram, pl.bf16, cur, use_poly ? 1.f : ns.b)) !=
           hipSuccess)
         return hip_fail(e, "launch Gram");
       t.done();
     }
     if (use_poly) {
       TimedLaunch t(MUON_K_POLY, stream);
-      if ((e = launch_poly(c, pl.totals[PH_SYM], pl.bf16, ns.b, ns.c)) != hipSuccess)
+      if ((e = launch_poly(c, pl.split_poly, pl.bf16, ns.b, ns.c)) != hipSuccess)
         return hip_fail(e, "launch polynomial");
       t.done();
     }
@@ -364,7 +411,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
     {
       TimedLaunch t(last ? MUON_K_PROD_FINISH : MUON_K_PROD, stream);
       const int32_t fin = !last ? FIN_NONE : ep.mode == MODE_STEP ? FIN_STEP : FIN_NS;
-      if ((e = launch_prod(c, pl.totals[PH_PROD], pl.bf16, cur, ns.a, use_poly, fin, ep.lr)) !=
+      if ((e = launch_prod(c, pl.split_prod, pl.bf16, cur, ns.a, use_poly, fin, ep.lr)) !=
           hipSuccess)
         return hip_fail(e, "launch product");
       t.done();

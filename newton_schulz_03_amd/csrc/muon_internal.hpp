@@ -23,6 +23,7 @@ constexpr int kEwTile = 64;         // tile side of the normalize / finish kerne
 constexpr int kThreads = 256;       // threads per block, every kernel
 constexpr int kReduceIters = 8;     // 16-byte vectors per thread per reduce block
 constexpr int kAlign = 256;         // workspace sub-buffer alignment
+constexpr int kXcd = 8;             // XCDs of the chip: workgroup b runs on XCD b % 8
 
 enum Phase : int { PH_REDUCE = 0, PH_NORMALIZE = 1, PH_SYM = 2, PH_PROD = 3, PH_FINISH = 4, NPHASE = 5 };
 enum Mode : int { MODE_NS = 0, MODE_STEP = 1 };
@@ -43,6 +44,14 @@ struct MatDesc {
   int32_t reserved;
   const void* u_src;          // STEP: where later kernels read the new momentum (mom, or mom_copy)
   void* mom_copy;             // STEP with the momentum in host memory: its device copy
+};
+
+// Tiles of one matrix-core launch, dealt to the XCDs in contiguous ranges cut
+// so that every XCD gets about the same number of K slices to run, not the
+// same number of tiles: in a ragged batch one tile can cost many times another.
+struct XcdSplit {
+  int32_t lo[kXcd + 1];  // XCD x takes tiles [lo[x], lo[x + 1]); lo[kXcd] = all tiles
+  int32_t grid;          // kXcd * the longest range: workgroups of a one-tile-each launch
 };
 
 struct LaunchCtx {
@@ -99,15 +108,16 @@ hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, cons
 hipError_t launch_finalize(const LaunchCtx& c, const ElemParams& p);
 hipError_t launch_normalize(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 hipError_t launch_finish(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
+// The matrix-core launches run the tiles that `sp` splits (sp.lo[kXcd] of them).
 // A = out_scale * X X^T  (out_scale = b when the polynomial has no A^2 term, else 1)
-hipError_t launch_gram(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
+hipError_t launch_gram(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur,
                        float out_scale);
 // B = b A + c A A  (c != 0)
-hipError_t launch_poly(const LaunchCtx& c, int32_t nblocks, bool is_bf16, float b, float cc);
+hipError_t launch_poly(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, float b, float cc);
 // X[next] = a X[cur] + Q X[cur] with Q = B (use_poly) or the already scaled A.
 // finish != 0 (bf16 only): the last product of the call, whose result goes to
 // the user's matrix (W - lr * scale * X', or the output) instead of X[next].
-hipError_t launch_prod(const LaunchCtx& c, int32_t nblocks, bool is_bf16, int32_t cur,
+hipError_t launch_prod(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur,
                        float a, bool use_poly, int32_t finish = 0, float lr = 0.f);
 
 }  // namespace muon

@@ -1,9 +1,10 @@
 """Summaries of rocprofv3 output for the Muon kernels, as short markdown.
 
 Usage:
-    python -m newton_schulz_03_amd.rocprof_summary trace DIR --command "..."
+    python -m newton_schulz_03_amd.rocprof_summary trace DIR --command "..." [--muon-only]
         DIR holds the CSV output of `rocprofv3 --kernel-trace --stats`:
-        a per-kernel table of calls and durations.
+        a per-kernel table of calls and durations (with --muon-only, of this
+        library's kernels alone).
     python -m newton_schulz_03_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
             --copy-bytes N --workload NAME --command "..."
         FETCH_DIR and WRITE_DIR hold the CSV output of two runs, one with
@@ -90,11 +91,22 @@ def counter_per_dispatch(d: str, counter: str):
     return {k: (len(disp[k]), tot[k] / max(1, len(disp[k]))) for k in tot}
 
 
+MUON_KERNELS = {name for _, name in SHORT_NAMES}
+
+
 def cmd_trace(a):
     rows = trace_table(a.dir)
+    if a.muon_only:
+        rows = [r for r in rows if r[0] in MUON_KERNELS]
+        tot = sum(r[4] for r in rows) or 1.0
+        rows = [r[:5] + (100.0 * r[4] / tot,) for r in rows]
     print(f"# Kernel trace: {a.title}\n")
     print(f"Command (from the repository root):\n\n```\n{a.command}\n```\n")
-    print("| kernel | calls | avg ms | total ms | % of GPU time |")
+    if a.muon_only:
+        print("Only this library's kernels are listed (the program's other kernels, such as input "
+              "generation, are left out); the last column is the share of their time.\n")
+    share = "% of listed time" if a.muon_only else "% of GPU time"
+    print(f"| kernel | calls | avg ms | total ms | {share} |")
     print("|---|---|---|---|---|")
     for short, _, calls, avg, total, pct in rows:
         print(f"| {short} | {calls} | {avg:.4f} | {total:.2f} | {pct:.1f} |")
@@ -164,6 +176,8 @@ def main(argv=None):
     t.add_argument("dir")
     t.add_argument("--title", default="")
     t.add_argument("--command", required=True)
+    t.add_argument("--muon-only", action="store_true",
+                   help="list this library's kernels only (drops input generation and the like)")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_dir")
     f.add_argument("write_dir")

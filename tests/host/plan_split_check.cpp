@@ -1,0 +1,135 @@
+// Host-only check of how the matrix-core launches deal tiles to the XCDs.
+//
+// Built with `hipcc --offload-host-only` against the ABI source itself, with
+// stub kernel launchers (no kernel is compiled or run).  For ragged batches of
+// random shapes it checks, for the Gram, A^2 and product launches of the plan:
+//   - the ranges start at 0, end at the launch's tile count and never shrink;
+//   - the grid is 8 times the longest range;
+//   - split_tile (the function the kernels call) maps the grid's workgroups
+//     onto every tile exactly once, the rest to -1;
+//   - every XCD's range holds at most 1/8 of the launch's work plus one tile.
+// Prints "OK <plans>" and exits 0, or names the first failure and exits 1.
+#include "muon_abi.hip"
+
+#include <random>
+
+namespace muon {
+hipError_t launch_reduce(const LaunchCtx&, int32_t, bool, const ElemParams&) { return hipSuccess; }
+hipError_t launch_finalize(const LaunchCtx&, const ElemParams&) { return hipSuccess; }
+hipError_t launch_normalize(const LaunchCtx&, int32_t, bool, const ElemParams&) {
+  return hipSuccess;
+}
+hipError_t launch_finish(const LaunchCtx&, int32_t, bool, const ElemParams&) { return hipSuccess; }
+hipError_t launch_gram(const LaunchCtx&, const XcdSplit&, bool, int32_t, float) {
+  return hipSuccess;
+}
+hipError_t launch_poly(const LaunchCtx&, const XcdSplit&, bool, float, float) {
+  return hipSuccess;
+}
+hipError_t launch_prod(const LaunchCtx&, const XcdSplit&, bool, int32_t, float, bool, int32_t,
+                       float) {
+  return hipSuccess;
+}
+hipError_t launch_adamw(const AdamCtx&, int32_t, bool, const AdamParams&) { return hipSuccess; }
+int64_t adamw_blocks(int64_t n) { return n; }
+}  // namespace muon
+
+using namespace muon;
+
+namespace {
+
+int failures = 0;
+
+void expect(bool ok, const char* what, int plan) {
+  if (!ok && failures++ == 0) std::printf("FAIL plan %d: %s\n", plan, what);
+}
+
+// tiles: per-matrix tile counts; slices: K slices per tile of each matrix
+void check_split(const XcdSplit& sp, const std::vector<int64_t>& tiles,
+                 const std::vector<int64_t>& slices, int plan) {
+  int64_t ntiles = 0;
+  for (int64_t t : tiles) ntiles += t;
+  expect(sp.lo[0] == 0 && sp.lo[kXcd] == ntiles, "ranges do not span the tiles", plan);
+  int64_t longest = 0;
+  for (int x = 0; x < kXcd; ++x) {
+    expect(sp.lo[x + 1] >= sp.lo[x], "ranges shrink", plan);
+    longest = std::max<int64_t>(longest, sp.lo[x + 1] - sp.lo[x]);
+  }
+  expect(sp.grid == kXcd * longest, "grid is not 8 x the longest range", plan);
+  std::vector<int> seen(ntiles, 0);
+  for (int32_t b = 0; b < sp.grid; ++b) {
+    const int32_t t = split_tile(sp, b);
+    if (t == -1) continue;
+    expect(t >= 0 && t < ntiles, "split_tile out of range", plan);
+    if (t >= 0 && t < ntiles) seen[t]++;
+  }
+  for (int64_t t = 0; t < ntiles; ++t) expect(seen[t] == 1, "a tile is not taken exactly once", plan);
+  // work per XCD: every boundary sits at the first tile whose preceding work
+  // reaches x/8 of the total, so no range exceeds 1/8 by a whole tile
+  std::vector<int64_t> cost;
+  int64_t total = 0, heaviest = 0;
+  for (size_t i = 0; i < tiles.size(); ++i)
+    for (int64_t k = 0; k < tiles[i]; ++k) {
+      cost.push_back(slices[i] + kTileOverheadSlices);
+      total += cost.back();
+      heaviest = std::max(heaviest, cost.back());
+    }
+  for (int x = 0; x < kXcd; ++x) {
+    int64_t w = 0;
+    for (int32_t t = sp.lo[x]; t < sp.lo[x + 1]; ++t) w += cost[t];
+    expect(kXcd * w < total + kXcd * heaviest, "an XCD gets more than 1/8 of the work + one tile",
+           plan);
+  }
+}
+
+}  // namespace
+
+int main() {
+  std::mt19937 rng(12345);
+  const int64_t dims[] = {1, 7, 255, 256, 257, 512, 1000, 1024, 2048, 4095, 6144, 8192};
+  int plans = 0;
+  for (int trial = 0; trial < 600; ++trial) {
+    const int batch = 1 + static_cast<int>(rng() % (trial < 500 ? 24 : 300));
+    std::vector<int64_t> r(batch), c(batch);
+    for (int i = 0; i < batch; ++i) {
+      r[i] = dims[rng() % 12];
+      c[i] = dims[rng() % 12];
+    }
+    Plan pl;
+    const int32_t dtype = (trial & 1) ? MUON_FP32 : MUON_BF16;
+    if (make_plan(batch, r.data(), c.data(), dtype, pl) != MUON_OK) {
+      expect(false, "make_plan failed", trial);
+      continue;
+    }
+    std::vector<int64_t> sym(batch), prod(batch), k_long(batch), k_short(batch);
+    for (int i = 0; i < batch; ++i) {
+      const int64_t ts = pl.desc[i].s_pad / kTile, tl = pl.desc[i].l_pad / kTile;
+      sym[i] = ts * (ts + 1) / 2;
+      prod[i] = ts * tl;
+      k_long[i] = pl.desc[i].l_pad / 32;
+      k_short[i] = pl.desc[i].s_pad / 32;
+    }
+    check_split(pl.split_gram, sym, k_long, trial);
+    check_split(pl.split_poly, sym, k_short, trial);
+    check_split(pl.split_prod, prod, k_short, trial);
+    ++plans;
+  }
+  // a uniform batch keeps equal ranges and one workgroup per tile
+  {
+    std::vector<int64_t> r(96, 2048), c(96, 6144);
+    Plan pl;
+    expect(make_plan(96, r.data(), c.data(), MUON_BF16, pl) == MUON_OK, "uniform plan", -1);
+    expect(pl.split_prod.grid == 18432 && pl.split_gram.grid == 3456, "uniform grid", -1);
+    for (int x = 0; x <= kXcd; ++x) expect(pl.split_prod.lo[x] == 2304 * x, "uniform ranges", -1);
+  }
+  // an empty batch launches nothing
+  {
+    Plan pl;
+    expect(make_plan(0, nullptr, nullptr, MUON_BF16, pl) == MUON_OK, "empty plan", -1);
+    expect(pl.split_gram.grid == 0 && pl.split_prod.grid == 0 && pl.split_prod.lo[kXcd] == 0,
+           "empty batch grid", -1);
+  }
+  if (failures) return 1;
+  std::printf("OK %d\n", plans);
+  return 0;
+}
