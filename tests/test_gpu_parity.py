@@ -76,6 +76,15 @@ def test_ns_ragged_batch(dtype):
     _ns_check(dtype, RAGGED)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ns_one_large_among_many_small(dtype):
+    """Tiles of very unequal cost in one launch: the XCD ranges, cut by work,
+    hold one-tile matrices on either side of a 48-tile one, and the grid has
+    about twice as many workgroups as tiles (the surplus exits at once)."""
+    shapes = [(64, 96)] * 20 + [(1536, 2048)] + [(96, 64)] * 20 + [(1024, 300)]
+    _ns_check(dtype, shapes)
+
+
 @pytest.mark.parametrize("coeffs,steps", [((1.0, 0.0, 0.0), 1), ((0.0, 1.0, 0.0), 1),
                                           ((0.0, 0.0, 1.0), 1), ((0.5, 0.25, -0.125), 2),
                                           (oracle.QUINTIC, 0)])
