@@ -42,14 +42,17 @@ def ns_flops(shape, steps, with_square=True):
     return steps * (gram + square + prod), steps * gram, steps * square, steps * prod
 
 
-def elementwise_bytes(shape, esize, call, nesterov):
-    """Algorithmic HBM bytes of the three bandwidth-bound kernels, per matrix."""
+def elementwise_bytes(shape, esize, call):
+    """Algorithmic HBM bytes of the two bandwidth-bound kernels, per matrix:
+    prepare (which writes U into the iterate, zero padded to 256 on both
+    sides) and finish."""
     n = shape[0] * shape[1] * esize
+    pad = -(-shape[0] // 256) * 256 * (-(-shape[1] // 256) * 256) * esize
     if call == "step":
-        # read G, M, write M';  read M' (and G), write X0;  read O, W, write W'
-        return 3 * n, (3 if nesterov else 2) * n, 3 * n
-    # read X;  read X, write X0;  read O, write out
-    return n, 2 * n, 2 * n
+        # read G, M, write M' and the iterate;  read O, W, write W'
+        return 3 * n + pad, 3 * n
+    # read X, write the iterate;  read O, write out
+    return n + pad, 2 * n
 
 
 def make_inputs(wl, device, threads=16):
@@ -456,19 +459,21 @@ def main(argv=None) -> int:
         ms, n = kern[name]
         return ms / n if n else float("nan")
 
-    prod_ms = avg("prod")
+    # the middle products (the first takes the norm factor, the last the update)
+    prod_ms = avg("prod") if kern["prod"][1] else avg("prod_first")
     achieved = alg_prod_launch / (prod_ms * 1e-3) / 1e12
     per_kernel = {k: {"avg_ms": round(avg(k), 4), "launches": kern[k][1]} for k in nsa.KERNELS
                   if kern[k][1]}
-    ns_ms = (kern["gram"][0] + kern["poly"][0] + kern["prod"][0] + kern["prod_finish"][0]) / args.steps
-    ew = [elementwise_bytes(s, esize, wl.call, wl.nesterov) for s in shapes]
-    for name, idx in (("reduce", 0), ("normalize", 1), ("finish", 2)):
+    ns_ms = sum(kern[k][0] for k in ("gram", "poly", "prod_first", "prod", "prod_finish")) / args.steps
+    ew = [elementwise_bytes(s, esize, wl.call) for s in shapes]
+    for name, idx in (("prepare", 0), ("finish", 1)):
         if name not in per_kernel:
             continue
         b = sum(e[idx] for e in ew)
         per_kernel[name]["gbs"] = round(b / (avg(name) * 1e-3) / 1e9, 1)
         per_kernel[name]["hbm_frac"] = round(b / (avg(name) * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
-    for name, flops in (("gram", alg_gram_launch), ("poly", alg_poly_launch), ("prod", alg_prod_launch)):
+    for name, flops in (("gram", alg_gram_launch), ("poly", alg_poly_launch), ("prod", alg_prod_launch),
+                        ("prod_first", alg_prod_launch)):
         if kern[name][1]:
             t = flops / (avg(name) * 1e-3) / 1e12
             per_kernel[name]["tflops"] = round(t, 1)

@@ -103,9 +103,8 @@ typedef struct {
  * 1T-parameter MoE on Europe's Jupiter supercomputer, and published the
  * recipe", §What moved the number, Offloading bullet).  Every m[i] must then be
  * pinned host memory (hipHostMalloc, or a pinned torch tensor); the step reads
- * M and writes the new momentum there in place, over the host link, once each,
- * and works from a device copy kept in the workspace.  Otherwise (0) m[i] are
- * device memory.
+ * M and writes the new momentum there in place, over the host link, once each.
+ * Otherwise (0) m[i] are device memory.
  */
 typedef struct {
   float lr;
@@ -199,15 +198,16 @@ int32_t muon_adamw_batched(int32_t batch, const int64_t* numel, void* const* p,
 
 /* Kernels of the step, for per-kernel timing. */
 typedef enum {
-  MUON_K_REDUCE = 0,    /* momentum and per-block sums of squares */
-  MUON_K_NORMALIZE = 1, /* X0 = U / (||U||_F + eps), short side first */
+  MUON_K_PREPARE = 0,   /* momentum, U into the iterate (short side first), sums of squares */
+  MUON_K_NORM = 1,      /* 1 / (||U||_F + eps) per matrix */
   MUON_K_GRAM = 2,      /* A = X X^T */
   MUON_K_POLY = 3,      /* B = b A + c A^2 */
-  MUON_K_PROD = 4,      /* X <- a X + B X */
+  MUON_K_PROD = 4,      /* X <- a X + B X, except the first and (bf16) the last */
   MUON_K_FINISH = 5,    /* W update, or the output copy (fp32, or no Newton-Schulz steps) */
   MUON_K_ADAMW = 6,     /* muon_adamw_batched */
   MUON_K_PROD_FINISH = 7, /* bf16: the last X <- a X + B X, writing W (or the output) itself */
-  MUON_K_COUNT = 8
+  MUON_K_PROD_FIRST = 8,  /* the first X <- a X + B X (its iterate is U, scaled as it is stored) */
+  MUON_K_COUNT = 9
 } muon_kernel;
 
 /*

@@ -26,7 +26,7 @@ EXPORTED = ("muon_workspace_bytes", "muon_ns_batched", "muon_step_batched",
             "muon_adamw_workspace_bytes", "muon_adamw_batched",
             "muon_status_string", "muon_last_error_detail", "muon_timing_enable",
             "muon_timing_read", "muon_timing_reset")
-KERNELS = ("reduce", "normalize", "gram", "poly", "prod", "finish", "adamw", "prod_finish")
+KERNELS = ("prepare", "norm", "gram", "poly", "prod", "finish", "adamw", "prod_finish", "prod_first")
 
 
 class MuonError(RuntimeError):

@@ -1,13 +1,16 @@
 // Bandwidth-bound kernels of the Muon step:
-//   k_reduce     momentum M' = beta*M + G (step) and per-block sums of U^2; with the
-//                momentum in host memory it also leaves a device copy of the new momentum
+//   k_prepare    momentum M' = beta*M + G (step) in the user's matrix, U = M' (or
+//                G + beta*M', Nesterov; x when only orthogonalizing) written once
+//                into the wide iterate, zero padded, and per-block sums of U^2
 //   k_finalize   1 / (||U||_F + eps) per matrix from those partials
-//   k_normalize  X0 = U / (||U||_F + eps) in the wide orientation, zero padded
 //   k_finish     W' = W - lr*sqrt(max(1,rows/cols))*O (step) or out = O (orthogonalize only)
-// All of them read and write whole 16-byte vectors along rows, so every
+// The iterate holds U itself, not X0 = U / (||U||_F + eps): the first Gram and
+// the first product take the factor into the scale they store with (the
+// finish pass, when there are no iterations), so U is read from HBM once.
+// Every kernel reads and writes whole 16-byte vectors along rows, so every
 // wavefront touches contiguous runs of memory, and each block issues all of its
 // loads before it waits on any of them: what keeps HBM busy is the number of
-// bytes in flight.  The norm is deterministic: each reduce block writes one
+// bytes in flight.  The norm is deterministic: each prepare block writes one
 // partial, and one finalize block per matrix sums them in a fixed order.
 #include "device_common.hpp"
 
@@ -15,49 +18,64 @@ namespace muon {
 
 namespace {
 
+// One 16-byte vector (V elements) of the user's matrix: the loads, then M', U
+// and the momentum store.
 template <typename T>
-struct URow {
-  // Loads 16 consecutive elements of U from user row `r`, starting at column c0,
-  // with zeros beyond the row.  U is x (orthogonalize only), M' (step), or
-  // G + beta*M' (Nesterov step).
-  static __device__ __forceinline__ void load(const MatDesc& d, const ElemParams& p, int64_t r,
-                                              int64_t c0, float* u) {
-    constexpr int V = Elt<T>::kVec;
-    const int64_t cols = d.cols;
-    const int64_t rowoff = r * cols;
-#pragma unroll
-    for (int q = 0; q < 16 / V; ++q) {
-      const int64_t col = c0 + q * V;
-      float* o = u + q * V;
-      if (d.vec_ok && col + V <= cols) {
-        const int64_t off = rowoff + col;
-        if (p.mode == MODE_NS) {
-          vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), o);
-        } else {
-          vec_to_f32<T>(ld16(static_cast<const T*>(d.u_src) + off), o);
-          if (p.nesterov) {
-            float g[V];
-            vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), g);
-#pragma unroll
-            for (int e = 0; e < V; ++e) o[e] = g[e] + p.beta * o[e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          float v = 0.f;
-          if (col + e < cols) {
-            const int64_t off = rowoff + col + e;
-            if (p.mode == MODE_NS) {
-              v = Elt<T>::to_f32(static_cast<const T*>(d.src)[off]);
-            } else {
-              v = Elt<T>::to_f32(static_cast<const T*>(d.u_src)[off]);
-              if (p.nesterov) v = Elt<T>::to_f32(static_cast<const T*>(d.src)[off]) + p.beta * v;
-            }
-          }
-          o[e] = v;
-        }
+struct UVec {
+  static constexpr int V = Elt<T>::kVec;
+  u32x4_t a, m;  // G (or x) and M
+  bool full;     // the whole vector lies in the matrix, 16-byte aligned
+
+  __device__ __forceinline__ void load(const MatDesc& d, const ElemParams& p, int64_t r,
+                                       int64_t c0) {
+    full = r < d.rows && d.vec_ok && c0 + V <= d.cols;
+    if (!full) return;
+    const int64_t off = r * d.cols + c0;
+    a = ld16(static_cast<const T*>(d.src) + off);
+    if (p.mode == MODE_STEP) m = ld16(static_cast<const T*>(d.mom) + off);
+  }
+
+  // u <- U over the vector (zeros outside the matrix); stores M' (step).  U is
+  // formed from the stored, rounded M', as the oracle's bf16 reading has it.
+  __device__ __forceinline__ void finish(const MatDesc& d, const ElemParams& p, int64_t r,
+                                         int64_t c0, float* u) const {
+    if (full) {
+      if (p.mode == MODE_NS) {
+        vec_to_f32<T>(a, u);
+        return;
       }
+      float g[V], mo[V], mn[V];
+      vec_to_f32<T>(a, g);
+      vec_to_f32<T>(m, mo);
+#pragma unroll
+      for (int e = 0; e < V; ++e) mn[e] = p.beta * mo[e] + g[e];
+      const u32x4_t packed = f32_to_vec<T>(mn);
+      st16(static_cast<T*>(d.mom) + r * d.cols + c0, packed);
+      vec_to_f32<T>(packed, u);
+      if (p.nesterov) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) u[e] = g[e] + p.beta * u[e];
+      }
+      return;
+    }
+    // an edge vector: element by element, clipped to the shape
+#pragma unroll
+    for (int e = 0; e < V; ++e) u[e] = 0.f;
+    if (r >= d.rows) return;
+    const int64_t off = r * d.cols;
+    const T* src = static_cast<const T*>(d.src) + off;
+    T* mom = static_cast<T*>(d.mom) + off;
+#pragma unroll 1
+    for (int e = 0; e < V && c0 + e < d.cols; ++e) {
+      const float g = Elt<T>::to_f32(src[c0 + e]);
+      if (p.mode == MODE_NS) {
+        u[e] = g;
+        continue;
+      }
+      const T stored = Elt<T>::from_f32(p.beta * Elt<T>::to_f32(mom[c0 + e]) + g);
+      mom[c0 + e] = stored;
+      const float mr = Elt<T>::to_f32(stored);
+      u[e] = p.nesterov ? g + p.beta * mr : mr;
     }
   }
 };
@@ -65,113 +83,95 @@ struct URow {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// k_reduce: one block per kThreads*V*kReduceIters elements of one matrix.
+// k_prepare: one block per 8192-element tile of the padded wide iterate: 32 x
+// 256 for a wide matrix, 64 x 128 (short side x long side) for a tall one,
+// which is read as the user's 128 x 64 tile and transposed through LDS.  Each
+// thread moves kVecs 16-byte vectors, vector v = it * 256 + threadIdx.x of the
+// tile in row-major order, so every load and store instruction of a wave
+// covers whole rows of the tile: contiguous runs of memory.  The transpose
+// holds U already rounded to T (the iterate's element type).
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_reduce(LaunchCtx c, ElemParams p) {
+__global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p) {
+  constexpr int V = Elt<T>::kVec;
+  constexpr int kVecs = kPrepTile / V / kThreads;  // 4 (bf16) or 8 (fp32)
+  constexpr int kTallRows = 2 * kEwTile, kTallCols = kEwTile;  // the user's tile of a tall matrix
+  constexpr int kPitch = kTallCols + 4 / static_cast<int>(sizeof(T));  // one 4-byte word of padding
+  __shared__ __attribute__((aligned(16))) T tile[kTallRows][kPitch];
   __shared__ float scratch[kThreads / 64];
   __shared__ int slot;
-  constexpr int V = Elt<T>::kVec;
-  constexpr int64_t kSpan = static_cast<int64_t>(kThreads) * V * kReduceIters;
-  const int32_t* pre = c.prefix + PH_REDUCE * (c.batch + 1);
+  const int32_t* pre = c.prefix + PH_PREPARE * (c.batch + 1);
   const int32_t b = blockIdx.x;
   const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, &slot));
   const MatDesc& d = c.desc[j];
-  const int64_t numel = d.numel;
-  const int64_t base = static_cast<int64_t>(b - pre[j]) * kSpan;
+  const int32_t t = b - pre[j];
+  const bool tall = d.tall != 0;
+  // tile origin in the wide iterate, and the row width (in vectors) of the tile as read
+  int64_t i0, j0;
+  int read_vpr;
+  if (!tall) {
+    const int32_t tpr = d.l_pad / kWideTileCols;
+    i0 = static_cast<int64_t>(t / tpr) * (kPrepTile / kWideTileCols);
+    j0 = static_cast<int64_t>(t % tpr) * kWideTileCols;
+    read_vpr = kWideTileCols / V;
+  } else {
+    const int32_t tpr = d.l_pad / kTallRows;
+    i0 = static_cast<int64_t>(t / tpr) * kTallCols;
+    j0 = static_cast<int64_t>(t % tpr) * kTallRows;
+    read_vpr = kTallCols / V;
+  }
+  // the user's (row, column) of each vector: wide (i0 + row, j0 + col); tall (j0 + row, i0 + col)
+  UVec<T> uv[kVecs];
+#pragma unroll
+  for (int it = 0; it < kVecs; ++it) {
+    const int v = it * kThreads + threadIdx.x;
+    const int row = v / read_vpr, col = (v % read_vpr) * V;
+    uv[it].load(d, p, (tall ? j0 : i0) + row, (tall ? i0 : j0) + col);
+  }
+  union Packed {
+    u32x4_t v;
+    T e[V];
+  } up[kVecs];  // U over each vector, rounded to T
   float acc = 0.f;
-  if (base + kSpan <= numel) {
-    // a whole span: all loads go out before the first store
-    const T* __restrict__ src = static_cast<const T*>(d.src) + base;
-    if (p.mode == MODE_NS) {
-      u32x4_t xv[kReduceIters];
 #pragma unroll
-      for (int it = 0; it < kReduceIters; ++it)
-        xv[it] = ld16(src + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * V);
+  for (int it = 0; it < kVecs; ++it) {
+    const int v = it * kThreads + threadIdx.x;
+    const int row = v / read_vpr, col = (v % read_vpr) * V;
+    float u[V];
+    uv[it].finish(d, p, (tall ? j0 : i0) + row, (tall ? i0 : j0) + col, u);
 #pragma unroll
-      for (int it = 0; it < kReduceIters; ++it) {
-        float u[V];
-        vec_to_f32<T>(xv[it], u);
+    for (int e = 0; e < V; ++e) acc += u[e] * u[e];
+    up[it].v = f32_to_vec<T>(u);
+  }
+  T* x0 = static_cast<T*>(iterate(d, 0));
+  if (!tall) {
+    // V consecutive columns starting at a multiple of V stay inside one slab row
 #pragma unroll
-        for (int e = 0; e < V; ++e) acc += u[e] * u[e];
-      }
-    } else {
-      T* __restrict__ mom = static_cast<T*>(d.mom) + base;
-      T* __restrict__ copy = d.mom_copy ? static_cast<T*>(d.mom_copy) + base : nullptr;
-      u32x4_t gv[kReduceIters], mv[kReduceIters];
-#pragma unroll
-      for (int it = 0; it < kReduceIters; ++it) {
-        const int64_t off = (static_cast<int64_t>(it) * kThreads + threadIdx.x) * V;
-        gv[it] = ld16(src + off);
-        mv[it] = ld16(mom + off);
-      }
-#pragma unroll
-      for (int it = 0; it < kReduceIters; ++it) {
-        const int64_t off = (static_cast<int64_t>(it) * kThreads + threadIdx.x) * V;
-        float g[V], m[V], mn[V], mr[V];
-        vec_to_f32<T>(gv[it], g);
-        vec_to_f32<T>(mv[it], m);
-#pragma unroll
-        for (int e = 0; e < V; ++e) mn[e] = p.beta * m[e] + g[e];
-        const u32x4_t packed = f32_to_vec<T>(mn);
-        st16(mom + off, packed);
-        if (copy) st16(copy + off, packed);
-        vec_to_f32<T>(packed, mr);  // U is formed from the stored (rounded) M', as later kernels do
-#pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const float u = p.nesterov ? g[e] + p.beta * mr[e] : mr[e];
-          acc += u * u;
-        }
-      }
+    for (int it = 0; it < kVecs; ++it) {
+      const int v = it * kThreads + threadIdx.x;
+      const int row = v / read_vpr, col = (v % read_vpr) * V;
+      st16(x0 + slab_off(i0 + row, j0 + col, d.l_pad), up[it].v);
     }
   } else {
-    // the matrix's last, partial span
-#pragma unroll 1
-    for (int it = 0; it < kReduceIters; ++it) {
-      const int64_t off = base + (static_cast<int64_t>(it) * kThreads + threadIdx.x) * V;
-      if (off >= numel) break;
-      const int n = (off + V <= numel) ? V : static_cast<int>(numel - off);
-      float u[V];
-      if (p.mode == MODE_NS) {
-        if (n == V) {
-          vec_to_f32<T>(ld16(static_cast<const T*>(d.src) + off), u);
-        } else {
-          for (int e = 0; e < V; ++e)
-            u[e] = e < n ? Elt<T>::to_f32(static_cast<const T*>(d.src)[off + e]) : 0.f;
-        }
-      } else {
-        float g[V], m[V];
-        T* mp = static_cast<T*>(d.mom) + off;
-        const T* gp = static_cast<const T*>(d.src) + off;
-        if (n == V) {
-          vec_to_f32<T>(ld16(gp), g);
-          vec_to_f32<T>(ld16(mp), m);
-        } else {
-          for (int e = 0; e < V; ++e) {
-            g[e] = e < n ? Elt<T>::to_f32(gp[e]) : 0.f;
-            m[e] = e < n ? Elt<T>::to_f32(mp[e]) : 0.f;
-          }
-        }
-        float mn[V];
 #pragma unroll
-        for (int e = 0; e < V; ++e) mn[e] = p.beta * m[e] + g[e];
-        u32x4_t packed = f32_to_vec<T>(mn);
-        float mr[V];
-        vec_to_f32<T>(packed, mr);
-        T* cp = d.mom_copy ? static_cast<T*>(d.mom_copy) + off : nullptr;
-        if (n == V) {
-          st16(mp, packed);
-          if (cp) st16(cp, packed);
-        } else {
-          for (int e = 0; e < n; ++e) mp[e] = Elt<T>::from_f32(mn[e]);
-          if (cp)
-            for (int e = 0; e < n; ++e) cp[e] = Elt<T>::from_f32(mn[e]);
-        }
+    for (int it = 0; it < kVecs; ++it) {
+      const int v = it * kThreads + threadIdx.x;
+      const int row = v / read_vpr, col = (v % read_vpr) * V;
 #pragma unroll
-        for (int e = 0; e < V; ++e) u[e] = p.nesterov ? g[e] + p.beta * mr[e] : mr[e];
-      }
+      for (int e = 0; e < V; ++e) tile[row][col + e] = up[it].e[e];
+    }
+    __syncthreads();
+    // the wide tile is kTallCols x kTallRows: vector v covers wide row v / wvpr,
+    // columns (v % wvpr) * V + 0..V-1, i.e. user rows of the tile at user column row
+    constexpr int wvpr = kTallRows / V;
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc += u[e] * u[e];
+    for (int it = 0; it < kVecs; ++it) {
+      const int v = it * kThreads + threadIdx.x;
+      const int wrow = v / wvpr, wcol = (v % wvpr) * V;
+      Packed o;
+#pragma unroll
+      for (int e = 0; e < V; ++e) o.e[e] = tile[wcol + e][wrow];
+      st16(x0 + slab_off(i0 + wrow, j0 + wcol, d.l_pad), o.v);
     }
   }
   const float total = block_sum(acc, scratch);
@@ -185,61 +185,12 @@ __global__ __launch_bounds__(kThreads) void k_reduce(LaunchCtx c, ElemParams p) 
 __global__ __launch_bounds__(kThreads) void k_finalize(LaunchCtx c, ElemParams p) {
   __shared__ double scratch[kThreads / 64];
   const int j = blockIdx.x;
-  const int32_t* pre = c.prefix + PH_REDUCE * (c.batch + 1);
+  const int32_t* pre = c.prefix + PH_PREPARE * (c.batch + 1);
   double s = 0.0;
   for (int32_t k = pre[j] + threadIdx.x; k < pre[j + 1]; k += kThreads) s += c.partials[k];
   s = block_sum(s, scratch);
   if (threadIdx.x == 0)
     c.inv_norm[j] = static_cast<float>(1.0 / (sqrt(s) + static_cast<double>(p.eps)));
-}
-
-// ---------------------------------------------------------------------------
-// k_normalize: one block per 64x64 tile of the padded wide iterate X0.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_normalize(LaunchCtx c, ElemParams p) {
-  __shared__ float tile[kEwTile][kEwTile + 1];
-  __shared__ int slot;
-  constexpr int V = Elt<T>::kVec;
-  const int32_t* pre = c.prefix + PH_NORMALIZE * (c.batch + 1);
-  const int32_t b = blockIdx.x;
-  const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, &slot));
-  const MatDesc& d = c.desc[j];
-  const int32_t t = b - pre[j];
-  const int32_t tpr = d.l_pad / kEwTile;
-  const int64_t i0 = static_cast<int64_t>(t / tpr) * kEwTile;  // wide rows
-  const int64_t j0 = static_cast<int64_t>(t % tpr) * kEwTile;  // wide cols
-  const int rr = threadIdx.x >> 2, cc = (threadIdx.x & 3) * 16;
-  float u[16];
-  if (!d.tall) {
-    if (i0 + rr < d.s) {
-      URow<T>::load(d, p, i0 + rr, j0 + cc, u);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) u[e] = 0.f;
-    }
-    const float inv = c.inv_norm[j];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) u[e] *= inv;
-  } else {
-    // wide X0[i][jw] = U[jw][i]: stage the user tile (rows j0.., cols i0..) through LDS
-    if (j0 + rr < d.l) {
-      URow<T>::load(d, p, j0 + rr, i0 + cc, u);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) u[e] = 0.f;
-    }
-    const float inv = c.inv_norm[j];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) tile[rr][cc + e] = u[e] * inv;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 16; ++e) u[e] = tile[cc + e][rr];
-  }
-  // 16 consecutive columns starting at a multiple of 16 stay inside one slab row
-  T* x0 = static_cast<T*>(iterate(d, 0)) + slab_off(i0 + rr, j0 + cc, d.l_pad);
-#pragma unroll
-  for (int q = 0; q < 16 / V; ++q) st16(x0 + q * V, f32_to_vec<T>(u + q * V));
 }
 
 // ---------------------------------------------------------------------------
@@ -288,6 +239,11 @@ __global__ __launch_bounds__(kThreads) void k_finish(LaunchCtx c, ElemParams p) 
     for (int e = 0; e < 16; ++e) o[e] = tile[cc + e][rr];
   }
   if (r >= d.rows) return;
+  if (p.scale_x) {
+    const float f = c.inv_norm[j];  // the iterate is U itself: O = X0 = f * U
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] *= f;
+  }
   const float step = p.lr * d.scale;
   if (vec_row) {
 #pragma unroll
@@ -329,27 +285,18 @@ __global__ __launch_bounds__(kThreads) void k_finish(LaunchCtx c, ElemParams p) 
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p) {
+hipError_t launch_prepare(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p) {
   if (nblocks <= 0) return hipSuccess;
   if (is_bf16)
-    hipLaunchKernelGGL(k_reduce<uint16_t>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+    hipLaunchKernelGGL(k_prepare<uint16_t>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
   else
-    hipLaunchKernelGGL(k_reduce<float>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
+    hipLaunchKernelGGL(k_prepare<float>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
   return hipGetLastError();
 }
 
 hipError_t launch_finalize(const LaunchCtx& c, const ElemParams& p) {
   if (c.batch <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_finalize, dim3(c.batch), dim3(kThreads), 0, c.stream, c, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_normalize(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p) {
-  if (nblocks <= 0) return hipSuccess;
-  if (is_bf16)
-    hipLaunchKernelGGL(k_normalize<uint16_t>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
-  else
-    hipLaunchKernelGGL(k_normalize<float>, dim3(nblocks), dim3(kThreads), 0, c.stream, c, p);
   return hipGetLastError();
 }
 

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
     }
     __syncthreads();
   }
-  gemm_store<T, MODE, true>(acc, tr, g);
+  gemm_store<T, MODE, true>(acc, tr, g, norm_factor<MODE>(c, g, tr));
 }
 
 namespace {
@@ -225,20 +225,20 @@ hipError_t launch_mode(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, Gem
 }  // namespace
 
 hipError_t launch_gram(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur,
-                       float out_scale) {
-  GemmArgs g{cur, 0.f, out_scale, 0, FIN_NONE, 0.f, 0, {}};
+                       float out_scale, bool first) {
+  GemmArgs g{cur, 0.f, out_scale, 0, FIN_NONE, 0.f, first ? 1 : 0, 0, {}};
   return launch_mode<GM_GRAM>(c, sp, is_bf16, g);
 }
 
 hipError_t launch_poly(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, float b, float cc) {
-  GemmArgs g{0, b / cc, cc, 0, FIN_NONE, 0.f, 0, {}};
+  GemmArgs g{0, b / cc, cc, 0, FIN_NONE, 0.f, 0, 0, {}};
   return launch_mode<GM_POLY>(c, sp, is_bf16, g);
 }
 
 hipError_t launch_prod(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur, float a,
-                       bool use_poly, int32_t finish, float lr) {
+                       bool use_poly, bool first, int32_t finish, float lr) {
   if (finish != FIN_NONE && !is_bf16) return hipErrorInvalidValue;  // fp32 keeps the finish kernel
-  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, finish, lr, 0, {}};
+  GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, finish, lr, first ? 1 : 0, 0, {}};
   return launch_mode<GM_PROD>(c, sp, is_bf16, g);
 }
 

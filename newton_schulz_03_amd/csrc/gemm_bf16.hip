@@ -238,16 +238,16 @@ struct FinalPiece {
 // the W pieces are loaded ahead in two halves, so that their latency hides
 // behind the staging and behind the first half's stores.
 template <bool TALL>
-__device__ __forceinline__ void store_final_interior(const f32x16_t (&acc)[4][4], uint16_t* base,
-                                                     int64_t cols, bool upd, float step,
-                                                     char* smem, int wave, int lane) {
+__device__ __forceinline__ void store_final_interior(const f32x16_t (&acc)[4][4], float nf,
+                                                     uint16_t* base, int64_t cols, bool upd,
+                                                     float step, char* smem, int wave, int lane) {
   using P = FinalPiece<TALL>;
   u32x4_t w[32];
   if (upd) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) w[u] = ld16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane));
   }
-  stage_tile(acc, 1.f, smem, wave, lane);
+  stage_tile(acc, nf, smem, wave, lane);
   if (upd) {
 #pragma unroll
     for (int u = 16; u < 32; ++u) w[u] = ld16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane));
@@ -270,13 +270,14 @@ __device__ __forceinline__ void store_final_interior(const f32x16_t (&acc)[4][4]
 // A tile on the matrix's edge: element by element where the 16-byte vector
 // does not fit, every piece clipped to the shape.
 template <bool TALL>
-__device__ __forceinline__ void store_final_edge(const f32x16_t (&acc)[4][4], const MatDesc& d,
-                                                 int64_t ur0, int64_t uc0, bool upd, float step,
-                                                 char* smem, int wave, int lane) {
+__device__ __forceinline__ void store_final_edge(const f32x16_t (&acc)[4][4], float nf,
+                                                 const MatDesc& d, int64_t ur0, int64_t uc0,
+                                                 bool upd, float step, char* smem, int wave,
+                                                 int lane) {
   using P = FinalPiece<TALL>;
   uint16_t* __restrict__ out = static_cast<uint16_t*>(d.dst);
   const int64_t rows = d.rows, cols = d.cols;
-  stage_tile(acc, 1.f, smem, wave, lane);
+  stage_tile(acc, nf, smem, wave, lane);
 #pragma unroll 1
   for (int u = 0; u < 32; ++u) {
     const int64_t r = ur0 + P::row(u, wave, lane), c = uc0 + P::col(u, wave, lane);
@@ -306,7 +307,8 @@ __device__ __forceinline__ void store_final_edge(const f32x16_t (&acc)[4][4], co
 // and the iterate is not stored.  T[q][p] = X'[ti*256 + q][tj*256 + p] is
 // staged in LDS as for the iterate.
 __device__ __forceinline__ void store_final(const f32x16_t (&acc)[4][4], const TileRef& tr,
-                                            const GemmArgs& g, char* smem, int wave, int lane) {
+                                            const GemmArgs& g, float nf, char* smem, int wave,
+                                            int lane) {
   const MatDesc& d = tr.d;
   const bool tall = d.tall != 0;
   const bool upd = g.finish == FIN_STEP;
@@ -317,22 +319,22 @@ __device__ __forceinline__ void store_final(const f32x16_t (&acc)[4][4], const T
   uint16_t* base = static_cast<uint16_t*>(d.dst) + ur0 * d.cols + uc0;
   if (interior) {
     if (tall)
-      store_final_interior<true>(acc, base, d.cols, upd, step, smem, wave, lane);
+      store_final_interior<true>(acc, nf, base, d.cols, upd, step, smem, wave, lane);
     else
-      store_final_interior<false>(acc, base, d.cols, upd, step, smem, wave, lane);
+      store_final_interior<false>(acc, nf, base, d.cols, upd, step, smem, wave, lane);
   } else {
     if (tall)
-      store_final_edge<true>(acc, d, ur0, uc0, upd, step, smem, wave, lane);
+      store_final_edge<true>(acc, nf, d, ur0, uc0, upd, step, smem, wave, lane);
     else
-      store_final_edge<false>(acc, d, ur0, uc0, upd, step, smem, wave, lane);
+      store_final_edge<false>(acc, nf, d, ur0, uc0, upd, step, smem, wave, lane);
   }
 }
 
 template <int MODE>
 __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], const TileRef& tr,
-                                               const GemmArgs& g, char* smem, int wave,
+                                               const GemmArgs& g, float nf, char* smem, int wave,
                                                int lane) {
-  stage_tile(acc, MODE == GM_PROD ? 1.f : g.out_scale, smem, wave, lane);
+  stage_tile(acc, MODE == GM_PROD ? nf : g.out_scale * nf, smem, wave, lane);
   const int t = threadIdx.x;
   // Rows of T: thread t moves chunk (t & 31) of rows (t >> 5) + 8u.
   {
@@ -380,8 +382,9 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
 }  // namespace
 
 // One output tile (tile number t of the launch).  FINAL (products only): the last product
-// of a call, storing with store_final.
-template <int MODE, bool FINAL>
+// of a call, storing with store_final.  FIRST (products only): the first product of a
+// call, whose iterate is still U, scaled by the norm factor as it is stored.
+template <int MODE, bool FINAL, bool FIRST>
 __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g, int32_t t,
                                           char* smem, int* slot) {
   const TileRef tr = decode_tile<MODE>(c, t, slot);
@@ -584,10 +587,13 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   }
   wait_vm<0>();  // no load may still target LDS: the ring is reused for the store
   __syncthreads();
+  // the norm factor: a product takes it only in its FIRST instantiation, so
+  // every other product stages with an exact 1 (no multiply)
+  const float nf = MODE == GM_PROD ? (FIRST ? c.inv_norm[tr.mat] : 1.f) : norm_factor<MODE>(c, g, tr);
   if constexpr (FINAL)
-    store_final(acc, tr, g, smem, wave, lane);
+    store_final(acc, tr, g, nf, smem, wave, lane);
   else
-    store_tile_lds<MODE>(acc, tr, g, smem, wave, lane);
+    store_tile_lds<MODE>(acc, tr, g, nf, smem, wave, lane);
 }
 
 // One block per CU, one tile per block, taken by split_tile: the XCDs get
@@ -596,30 +602,38 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
 // each XCD walks one contiguous range of equal length.  The loop is a separate
 // instantiation: across tiles the compiler keeps tile-invariant values in
 // registers, which the single-tile kernel cannot spare.
-template <int MODE, bool FINAL, bool LOOP>
+template <int MODE, bool FINAL, bool LOOP, bool FIRST>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDSB];
   __shared__ int slot;
   if constexpr (LOOP) {
     for (int32_t v = blockIdx.x; v < g.ntiles; v += gridDim.x) {
-      gemm_tile<MODE, FINAL>(c, g, xcd_remap(v, g.ntiles), smem, &slot);
+      gemm_tile<MODE, FINAL, FIRST>(c, g, xcd_remap(v, g.ntiles), smem, &slot);
       __syncthreads();  // every wave is done with LDS before the next tile's loads land there
     }
   } else {
     const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
     if (t < 0) return;  // the whole block: t depends on blockIdx.x only
-    gemm_tile<MODE, FINAL>(c, g, t, smem, &slot);
+    gemm_tile<MODE, FINAL, FIRST>(c, g, t, smem, &slot);
   }
 }
 
-template <int MODE, bool FINAL>
+template <int MODE, bool FINAL, bool FIRST>
 void launch_one(const LaunchCtx& c, int32_t nblocks, bool loop, const GemmArgs& g) {
   if (loop)
-    hipLaunchKernelGGL((k_gemm_bf16<MODE, FINAL, true>), dim3(nblocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_gemm_bf16<MODE, FINAL, true, FIRST>), dim3(nblocks), dim3(kThreads), 0,
                        c.stream, c, g);
   else
-    hipLaunchKernelGGL((k_gemm_bf16<MODE, FINAL, false>), dim3(nblocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_gemm_bf16<MODE, FINAL, false, FIRST>), dim3(nblocks), dim3(kThreads), 0,
                        c.stream, c, g);
+}
+
+template <bool FINAL>
+void launch_prod_bf16(const LaunchCtx& c, int32_t nblocks, bool loop, const GemmArgs& g) {
+  if (g.first)
+    launch_one<GM_PROD, FINAL, true>(c, nblocks, loop, g);
+  else
+    launch_one<GM_PROD, FINAL, false>(c, nblocks, loop, g);
 }
 
 // g.split.grid workgroups of one tile each or, with loop, nblocks workgroups
@@ -628,13 +642,13 @@ hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, bool 
                             const GemmArgs& g) {
   if (nblocks <= 0) return hipSuccess;
   switch (mode) {
-    case GM_GRAM: launch_one<GM_GRAM, false>(c, nblocks, loop, g); break;
-    case GM_POLY: launch_one<GM_POLY, false>(c, nblocks, loop, g); break;
+    case GM_GRAM: launch_one<GM_GRAM, false, false>(c, nblocks, loop, g); break;
+    case GM_POLY: launch_one<GM_POLY, false, false>(c, nblocks, loop, g); break;
     default:
       if (g.finish != FIN_NONE)
-        launch_one<GM_PROD, true>(c, nblocks, loop, g);
+        launch_prod_bf16<true>(c, nblocks, loop, g);
       else
-        launch_one<GM_PROD, false>(c, nblocks, loop, g);
+        launch_prod_bf16<false>(c, nblocks, loop, g);
       break;
   }
   return hipGetLastError();

@@ -20,6 +20,9 @@ enum GemmMode : int { GM_GRAM = 0, GM_POLY = 1, GM_PROD = 2 };
 //   GRAM  acc = X X^T,            A  = out_scale * acc   (out_scale = b when c = 0, else 1)
 //   POLY  acc = A A + s A,        B  = c * acc = b A + c A A   (s = b/c)
 //   PROD  acc = Q X + s X,        X' = acc                     (s = a)
+// In the first iteration X holds U = (||U||_F + eps) X0, so the Gram stores
+// f^2 * out_scale * acc and the product f * acc, f = 1 / (||U||_F + eps)
+// (norm_factor); the iteration then runs on X0 exactly as written above.
 // The s-multiple of the source tile is added inside the K loop by the bf16
 // kernel (matrix cores, see gemm_bf16.hip) and at store time by the fp32 one.
 // The last product of a call can hand its result straight to the user's
@@ -34,6 +37,7 @@ struct GemmArgs {
   int32_t use_poly;   // PROD: Q = B (1) or A (0)
   int32_t finish;     // PROD: FinishMode
   float lr;           // PROD with FIN_STEP: learning rate
+  int32_t first;      // GRAM, PROD: X[cur] holds U; scale by f^2 (GRAM) or f (PROD), f = inv_norm
   int32_t ntiles;     // tiles of the launch
   XcdSplit split;     // one tile per workgroup: which tile workgroup b takes (split_tile)
 };
@@ -83,8 +87,19 @@ __device__ __forceinline__ void sym_tile(int32_t t, int32_t T, int32_t& ti, int3
 
 struct TileRef {
   MatDesc d;  // a register copy: the epilogue's stores cannot alias it
+  int32_t mat;  // index of the matrix in the batch
   int32_t ti, tj;
 };
+
+// Extra factor of the stored result (see the table at GemmArgs): f^2 for the
+// first Gram, f for the first product, 1 otherwise.
+template <int MODE>
+__device__ __forceinline__ float norm_factor(const LaunchCtx& c, const GemmArgs& g,
+                                             const TileRef& tr) {
+  if (MODE == GM_POLY || !g.first) return 1.f;
+  const float f = c.inv_norm[tr.mat];
+  return MODE == GM_GRAM ? f * f : f;
+}
 
 // Tile of workgroup b in a launch of one tile per workgroup: b runs on XCD
 // x = b % 8 and takes the (b / 8)-th tile of that XCD's range; -1 past its end
@@ -111,6 +126,7 @@ __device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int32_t b, in
   const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;
   r.d = c.desc[j];
+  r.mat = j;
   const int32_t t = b - pre[j];
   const int32_t ts = r.d.s_pad / kTile;
   if constexpr (MODE == GM_PROD) {
@@ -154,7 +170,7 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 // the polynomial); it is read and added here, one row of blocks at a time.
 template <typename T, int MODE, bool ADD_TERM>
 __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const TileRef& tr,
-                                           const GemmArgs& g) {
+                                           const GemmArgs& g, float nf) {
   const LanePos lp = lane_pos(tr);
   const int64_t s_pad = tr.d.s_pad, l_pad = tr.d.l_pad;
   if constexpr (MODE == GM_PROD) {
@@ -179,6 +195,7 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
           for (int e = 0; e < 4; ++e) {
             v[e] = acc[mi][ni][4 * gg + e];
             if constexpr (ADD_TERM) v[e] += g.init_scale * x[ni][gg][e];
+            v[e] *= nf;
           }
           store4<T>(xout + slab_off(lp.row0 + ni * 32, lp.col0 + mi * 32 + 8 * gg, l_pad), v);
         }
@@ -209,7 +226,7 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[4][4], const Ti
           for (int e = 0; e < 4; ++e) {
             float t = acc[mi][ni][4 * gg + e];
             if constexpr (ADD_TERM && MODE == GM_POLY) t += g.init_scale * av[ni][gg][e];
-            v[e] = g.out_scale * t;
+            v[e] = g.out_scale * nf * t;
           }
           const int64_t rq = lp.rq0 + ni * 32, cp = lp.cp0 + mi * 32 + 8 * gg;
           store4<T>(out + slab_off(rq, cp, s_pad), v);

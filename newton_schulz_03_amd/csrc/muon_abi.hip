@@ -41,7 +41,7 @@ struct Plan {
   std::vector<MatDesc> desc;        // workspace pointers filled in by bind()
   std::vector<size_t> mat_off;      // byte offset of matrix i's buffers
   std::vector<int32_t> prefix;      // NPHASE x (batch + 1)
-  int32_t totals[NPHASE] = {0, 0, 0, 0, 0};
+  int32_t totals[NPHASE] = {0, 0, 0, 0};
   XcdSplit split_gram{}, split_poly{}, split_prod{};  // matrix-core launches over the XCDs
   size_t table_bytes = 0;
   size_t inv_off = 0;
@@ -95,11 +95,10 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
   pl.bf16 = dtype == MUON_BF16;
   pl.esize = pl.bf16 ? 2 : 4;
   const int64_t vec = 16 / static_cast<int64_t>(pl.esize);
-  const int64_t reduce_elems = static_cast<int64_t>(kThreads) * vec * kReduceIters;
   pl.desc.assign(batch, MatDesc{});
   pl.mat_off.assign(batch, 0);
   pl.prefix.assign(static_cast<size_t>(NPHASE) * (batch + 1), 0);
-  int64_t tot[NPHASE] = {0, 0, 0, 0, 0};
+  int64_t tot[NPHASE] = {0, 0, 0, 0};
   // per matrix: symmetric and product tiles; K slices of the Gram (long side)
   // and of A^2 and the product (short side)
   std::vector<int64_t> sym_cnt(batch), prod_cnt(batch), k_long(batch), k_short(batch);
@@ -124,11 +123,10 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
     d.scale = static_cast<float>(std::sqrt(std::max(1.0, static_cast<double>(r) / static_cast<double>(c))));
     const int64_t ts = d.s_pad / kTile, tl = d.l_pad / kTile;
     const int64_t cnt[NPHASE] = {
-        cdiv(d.numel, reduce_elems),                                   // PH_REDUCE
-        static_cast<int64_t>(d.s_pad / kEwTile) * (d.l_pad / kEwTile),  // PH_NORMALIZE
-        ts * (ts + 1) / 2,                                             // PH_SYM
-        ts * tl,                                                       // PH_PROD
-        cdiv(r, kEwTile) * cdiv(c, kEwTile),                           // PH_FINISH
+        static_cast<int64_t>(d.s_pad) * d.l_pad / kPrepTile,                  // PH_PREPARE
+        ts * (ts + 1) / 2,                                                   // PH_SYM
+        ts * tl,                                                             // PH_PROD
+        cdiv(r, kEwTile) * cdiv(c, kEwTile),                                 // PH_FINISH
     };
     sym_cnt[i] = cnt[PH_SYM];
     prod_cnt[i] = cnt[PH_PROD];
@@ -156,7 +154,7 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
   pl.inv_off = off;
   off += align_up(sizeof(float) * static_cast<size_t>(batch), kAlign);
   pl.partials_off = off;
-  off += align_up(sizeof(float) * static_cast<size_t>(tot[PH_REDUCE]), kAlign);
+  off += align_up(sizeof(float) * static_cast<size_t>(tot[PH_PREPARE]), kAlign);
   for (int32_t i = 0; i < batch; ++i) {
     const MatDesc& d = pl.desc[i];
     pl.mat_off[i] = off;
@@ -377,16 +375,14 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   c.stream = stream;
   hipError_t e;
   {
-    TimedLaunch t(MUON_K_REDUCE, stream);
-    if ((e = launch_reduce(c, pl.totals[PH_REDUCE], pl.bf16, ep)) != hipSuccess)
-      return hip_fail(e, "launch momentum/sum-of-squares");
+    TimedLaunch t(MUON_K_PREPARE, stream);
+    if ((e = launch_prepare(c, pl.totals[PH_PREPARE], pl.bf16, ep)) != hipSuccess)
+      return hip_fail(e, "launch momentum/iterate/sum-of-squares");
     t.done();
   }
   {
-    TimedLaunch t(MUON_K_NORMALIZE, stream);
+    TimedLaunch t(MUON_K_NORM, stream);
     if ((e = launch_finalize(c, ep)) != hipSuccess) return hip_fail(e, "launch norm finalize");
-    if ((e = launch_normalize(c, pl.totals[PH_NORMALIZE], pl.bf16, ep)) != hipSuccess)
-      return hip_fail(e, "launch normalize");
     t.done();
   }
   const bool use_poly = ns.c != 0.f;
@@ -396,7 +392,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   for (int k = 0; k < ns.steps; ++k) {
     {
       TimedLaunch t(MUON_K_GRAM, stream);
-      if ((e = launch_gram(c, pl.split_gram, pl.bf16, cur, use_poly ? 1.f : ns.b)) !=
+      if ((e = launch_gram(c, pl.split_gram, pl.bf16, cur, use_poly ? 1.f : ns.b, k == 0)) !=
           hipSuccess)
         return hip_fail(e, "launch Gram");
       t.done();
@@ -409,10 +405,10 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
     }
     const bool last = fused && k + 1 == ns.steps;
     {
-      TimedLaunch t(last ? MUON_K_PROD_FINISH : MUON_K_PROD, stream);
+      TimedLaunch t(last ? MUON_K_PROD_FINISH : k == 0 ? MUON_K_PROD_FIRST : MUON_K_PROD, stream);
       const int32_t fin = !last ? FIN_NONE : ep.mode == MODE_STEP ? FIN_STEP : FIN_NS;
-      if ((e = launch_prod(c, pl.split_prod, pl.bf16, cur, ns.a, use_poly, fin, ep.lr)) !=
-          hipSuccess)
+      if ((e = launch_prod(c, pl.split_prod, pl.bf16, cur, ns.a, use_poly, k == 0, fin,
+                           ep.lr)) != hipSuccess)
         return hip_fail(e, "launch product");
       t.done();
     }
@@ -421,6 +417,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   if (fused) return MUON_OK;
   ElemParams fp = ep;
   fp.cur = cur;
+  fp.scale_x = ns.steps == 0 ? 1 : 0;  // no product took the norm factor
   {
     TimedLaunch t(MUON_K_FINISH, stream);
     if ((e = launch_finish(c, pl.totals[PH_FINISH], pl.bf16, fp)) != hipSuccess)
@@ -514,9 +511,8 @@ extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const i
       pl.desc[i].src = g[i];
       pl.desc[i].dst = w[i];
       if (p->momentum_host) {
-        // pinned host memory: the kernels use its device mapping, and the new
-        // momentum is also copied into the second iterate buffer, which nothing
-        // uses before the first product
+        // pinned host memory: the prepare kernel reads M and writes M' through
+        // its device mapping, once each; U goes to the iterate in HBM
         hipPointerAttribute_t attr{};
         hipError_t e = hipPointerGetAttributes(&attr, m[i]);
         if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
@@ -527,12 +523,8 @@ extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const i
         if (!aligned16(attr.devicePointer))
           return fail(MUON_ERR_INVALID_ARG, "matrix %d: device mapping of m not 16-byte aligned", i);
         pl.desc[i].mom = attr.devicePointer;
-        pl.desc[i].mom_copy = pl.desc[i].x[1];
-        pl.desc[i].u_src = pl.desc[i].x[1];
       } else {
         pl.desc[i].mom = m[i];
-        pl.desc[i].mom_copy = nullptr;
-        pl.desc[i].u_src = m[i];
       }
     }
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -3,8 +3,10 @@
 // Workspace layout, per call (offsets from the caller's 256-byte aligned base):
 //   [table]     MatDesc[batch], then the phase prefix arrays int32[NPHASE][batch+1]
 //   [inv]       float[batch]: 1 / (||U||_F + eps) per matrix
-//   [partials]  float[reduce blocks]: per-block sums of squares (Frobenius norm)
+//   [partials]  float[prepare blocks]: per-block sums of squares (Frobenius norm)
 //   per matrix  X ping, X pong: s_pad x l_pad;  A (Gram), B (polynomial): s_pad x s_pad
+// X ping starts out holding U itself; the first Gram and product scale by the
+// norm factor.
 // Every matrix is held in its wide orientation (short side first): a matrix
 // with more rows than columns is transposed on the way in and back on the way
 // out.  s_pad and l_pad round the short and long sides up to the GEMM tile
@@ -19,13 +21,14 @@
 namespace muon {
 
 constexpr int kTile = 256;          // GEMM output tile (both sides) and padding granularity
-constexpr int kEwTile = 64;         // tile side of the normalize / finish kernels
+constexpr int kEwTile = 64;         // tile side of the finish kernel (and of prepare's tall tiles)
+constexpr int kPrepTile = 8192;     // elements per prepare block: 32 x 256 (wide) or 64 x 128 (tall)
+constexpr int kWideTileCols = 256;  // long-side width of prepare's wide tiles
 constexpr int kThreads = 256;       // threads per block, every kernel
-constexpr int kReduceIters = 8;     // 16-byte vectors per thread per reduce block
 constexpr int kAlign = 256;         // workspace sub-buffer alignment
 constexpr int kXcd = 8;             // XCDs of the chip: workgroup b runs on XCD b % 8
 
-enum Phase : int { PH_REDUCE = 0, PH_NORMALIZE = 1, PH_SYM = 2, PH_PROD = 3, PH_FINISH = 4, NPHASE = 5 };
+enum Phase : int { PH_PREPARE = 0, PH_SYM = 1, PH_PROD = 2, PH_FINISH = 3, NPHASE = 4 };
 enum Mode : int { MODE_NS = 0, MODE_STEP = 1 };
 
 struct MatDesc {
@@ -42,8 +45,6 @@ struct MatDesc {
   int32_t vec_ok;             // cols is a multiple of the 16-byte vector width
   float scale;                // sqrt(max(1, rows/cols))
   int32_t reserved;
-  const void* u_src;          // STEP: where later kernels read the new momentum (mom, or mom_copy)
-  void* mom_copy;             // STEP with the momentum in host memory: its device copy
 };
 
 // Tiles of one matrix-core launch, dealt to the XCDs in contiguous ranges cut
@@ -71,6 +72,7 @@ struct ElemParams {
   float eps;
   float lr;
   int32_t cur;       // which X buffer holds the final iterate (finish)
+  int32_t scale_x;   // finish: the iterate is still U (no iterations): scale by the norm factor
 };
 
 // AdamW over a ragged batch of flat tensors.
@@ -102,22 +104,24 @@ int64_t adamw_blocks(int64_t numel);
 hipError_t launch_adamw(const AdamCtx& c, int32_t nblocks, bool is_bf16, const AdamParams& a);
 
 // Host launchers (one per kernel family).  is_bf16 selects the element type.
-hipError_t launch_reduce(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
-// One block per matrix: 1 / (||U||_F + eps) from the reduce partials, summed in a
+// Momentum (step), U into X ping and the per-block sums of U^2.
+hipError_t launch_prepare(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
+// One block per matrix: 1 / (||U||_F + eps) from the prepare partials, summed in a
 // fixed order in double.
 hipError_t launch_finalize(const LaunchCtx& c, const ElemParams& p);
-hipError_t launch_normalize(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 hipError_t launch_finish(const LaunchCtx& c, int32_t nblocks, bool is_bf16, const ElemParams& p);
 // The matrix-core launches run the tiles that `sp` splits (sp.lo[kXcd] of them).
+// `first`: X[cur] still holds U, so the result takes the norm factor
+// f = 1 / (||U||_F + eps) of its matrix (f^2 for the Gram).
 // A = out_scale * X X^T  (out_scale = b when the polynomial has no A^2 term, else 1)
 hipError_t launch_gram(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur,
-                       float out_scale);
+                       float out_scale, bool first);
 // B = b A + c A A  (c != 0)
 hipError_t launch_poly(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, float b, float cc);
 // X[next] = a X[cur] + Q X[cur] with Q = B (use_poly) or the already scaled A.
 // finish != 0 (bf16 only): the last product of the call, whose result goes to
 // the user's matrix (W - lr * scale * X', or the output) instead of X[next].
 hipError_t launch_prod(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur,
-                       float a, bool use_poly, int32_t finish = 0, float lr = 0.f);
+                       float a, bool use_poly, bool first, int32_t finish = 0, float lr = 0.f);
 
 }  // namespace muon

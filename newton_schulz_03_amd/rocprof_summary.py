@@ -32,13 +32,19 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_common.hpp",
                   "csrc/muon_internal.hpp")
 
-SHORT_NAMES = (("k_gemm_bf16<0,false,false>", "gram"), ("k_gemm_bf16<1,false,false>", "poly"),
-               ("k_gemm_bf16<2,false,false>", "prod"), ("k_gemm_bf16<2,true,false>", "prod_finish"),
-               ("k_gemm_bf16<0,false,true>", "gram_budget"), ("k_gemm_bf16<1,false,true>", "poly_budget"),
-               ("k_gemm_bf16<2,false,true>", "prod_budget"),
-               ("k_gemm_bf16<2,true,true>", "prod_finish_budget"),
-               ("k_gemm_staged", "gemm_fp32"), ("k_reduce", "reduce"), ("k_normalize", "normalize"),
-               ("k_finish", "finish"), ("k_finalize", "finalize"), ("k_adamw", "adamw"))
+SHORT_NAMES = (("k_gemm_bf16<0,false,false,false>", "gram"), ("k_gemm_bf16<1,false,false,false>", "poly"),
+               ("k_gemm_bf16<2,false,false,false>", "prod"),
+               ("k_gemm_bf16<2,false,false,true>", "prod_first"),
+               ("k_gemm_bf16<2,true,false,false>", "prod_finish"),
+               ("k_gemm_bf16<2,true,false,true>", "prod_finish_first"),
+               ("k_gemm_bf16<0,false,true,false>", "gram_budget"),
+               ("k_gemm_bf16<1,false,true,false>", "poly_budget"),
+               ("k_gemm_bf16<2,false,true,false>", "prod_budget"),
+               ("k_gemm_bf16<2,false,true,true>", "prod_first_budget"),
+               ("k_gemm_bf16<2,true,true,false>", "prod_finish_budget"),
+               ("k_gemm_bf16<2,true,true,true>", "prod_finish_first_budget"),
+               ("k_gemm_staged", "gemm_fp32"), ("k_prepare", "prepare"), ("k_finish", "finish"),
+               ("k_finalize", "norm"), ("k_adamw", "adamw"))
 
 
 def kernel_source_digest() -> str:

@@ -14,20 +14,17 @@
 #include <random>
 
 namespace muon {
-hipError_t launch_reduce(const LaunchCtx&, int32_t, bool, const ElemParams&) { return hipSuccess; }
+hipError_t launch_prepare(const LaunchCtx&, int32_t, bool, const ElemParams&) { return hipSuccess; }
 hipError_t launch_finalize(const LaunchCtx&, const ElemParams&) { return hipSuccess; }
-hipError_t launch_normalize(const LaunchCtx&, int32_t, bool, const ElemParams&) {
-  return hipSuccess;
-}
 hipError_t launch_finish(const LaunchCtx&, int32_t, bool, const ElemParams&) { return hipSuccess; }
-hipError_t launch_gram(const LaunchCtx&, const XcdSplit&, bool, int32_t, float) {
+hipError_t launch_gram(const LaunchCtx&, const XcdSplit&, bool, int32_t, float, bool) {
   return hipSuccess;
 }
 hipError_t launch_poly(const LaunchCtx&, const XcdSplit&, bool, float, float) {
   return hipSuccess;
 }
-hipError_t launch_prod(const LaunchCtx&, const XcdSplit&, bool, int32_t, float, bool, int32_t,
-                       float) {
+hipError_t launch_prod(const LaunchCtx&, const XcdSplit&, bool, int32_t, float, bool, bool,
+                       int32_t, float) {
   return hipSuccess;
 }
 hipError_t launch_adamw(const AdamCtx&, int32_t, bool, const AdamParams&) { return hipSuccess; }

@@ -33,6 +33,15 @@ def test_every_declared_function_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_kernel_names_follow_the_header_enum():
+    text = open(nsa.HEADER_PATH).read()
+    ids = {m.group(1).lower(): int(m.group(2))
+           for m in re.finditer(r"MUON_K_([A-Z_]+)\s*=\s*(\d+)", text)}
+    count = ids.pop("count")
+    assert count == len(nsa.KERNELS)
+    assert {name: k for k, name in enumerate(nsa.KERNELS)} == ids
+
+
 def test_status_strings(lib):
     for code, name in [(0, "MUON_OK"), (1, "MUON_ERR_INVALID_ARG"), (2, "MUON_ERR_UNSUPPORTED"),
                        (3, "MUON_ERR_WORKSPACE"), (4, "MUON_ERR_HIP")]:
@@ -46,11 +55,11 @@ def expected_workspace(shapes, esize):
         return (x + a - 1) // a * a
 
     batch = len(shapes)
-    desc = 128  # sizeof(MatDesc)
-    total = up(desc * batch, 256) + up(4 * 5 * (batch + 1), 256)
+    desc = 112  # sizeof(MatDesc)
+    total = up(desc * batch, 256) + up(4 * 4 * (batch + 1), 256)  # 4 phase prefix arrays
     total += up(4 * batch, 256)  # per-matrix 1 / (||U|| + eps)
-    vec = 16 // esize
-    blocks = sum(-(-r * c // (256 * vec * 8)) for r, c in shapes)
+    # one partial sum of squares per 64 x 128 tile of the padded wide iterate
+    blocks = sum((up(min(r, c), 256) // 64) * (up(max(r, c), 256) // 128) for r, c in shapes)
     total += up(4 * blocks, 256)
     for r, c in shapes:
         s, l = min(r, c), max(r, c)

@@ -85,6 +85,43 @@ def test_ns_one_large_among_many_small(dtype):
     _ns_check(dtype, shapes)
 
 
+@pytest.mark.parametrize("dtype,steps,call", [("bf16", 5, "step"), ("bf16", 1, "ns"),
+                                             ("fp32", 5, "step"), ("bf16", 0, "step"),
+                                             ("fp32", 0, "ns")])
+def test_launch_sequence(dtype, steps, call):
+    """Which kernels one call launches: the first product takes the norm factor
+    (its iterate is U), bf16 fuses the update into the last product, fp32 and
+    zero iterations end with the finish pass."""
+    wl = _wl("muon" if call == "step" else "gauss", dtype, [(300, 700), (700, 300)], steps=steps)
+    ins = device_inputs(wl)
+    torch.cuda.synchronize()
+    nsa.timing_reset()
+    nsa.timing_enable(True)
+    try:
+        if call == "step":
+            nsa.step_batched([d["w"] for d in ins], [d["g"] for d in ins], [d["m"] for d in ins],
+                             steps=steps)
+        else:
+            nsa.ns_batched([d["x"] for d in ins], steps=steps)
+        torch.cuda.synchronize()
+    finally:
+        nsa.timing_enable(False)
+    got = {k: n for k, (_, n) in nsa.timing_read().items() if n}
+    fused = dtype == "bf16" and steps > 0
+    want = {"prepare": 1, "norm": 1}
+    if steps:
+        want.update(gram=steps, poly=steps)
+        want["prod_finish" if fused and steps == 1 else "prod_first"] = 1
+        middle = steps - 1 - (1 if fused and steps > 1 else 0)
+        if middle:
+            want["prod"] = middle
+        if fused and steps > 1:
+            want["prod_finish"] = 1
+    if not fused:
+        want["finish"] = 1
+    assert got == want
+
+
 @pytest.mark.parametrize("coeffs,steps", [((1.0, 0.0, 0.0), 1), ((0.0, 1.0, 0.0), 1),
                                           ((0.0, 0.0, 1.0), 1), ((0.5, 0.25, -0.125), 2),
                                           (oracle.QUINTIC, 0)])
