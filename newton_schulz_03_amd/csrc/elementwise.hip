@@ -143,14 +143,14 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
     for (int e = 0; e < V; ++e) acc += u[e] * u[e];
     up[it].v = f32_to_vec<T>(u);
   }
-  T* x0 = static_cast<T*>(iterate(d, 0));
+  T* xu = static_cast<T*>(iterate(d, 0));  // the first iterate buffer, holding U
   if (!tall) {
     // V consecutive columns starting at a multiple of V stay inside one slab row
 #pragma unroll
     for (int it = 0; it < kVecs; ++it) {
       const int v = it * kThreads + threadIdx.x;
       const int row = v / read_vpr, col = (v % read_vpr) * V;
-      st16(x0 + slab_off(i0 + row, j0 + col, d.l_pad), up[it].v);
+      st16(xu + slab_off(i0 + row, j0 + col, d.l_pad), up[it].v);
     }
   } else {
 #pragma unroll
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
       Packed o;
 #pragma unroll
       for (int e = 0; e < V; ++e) o.e[e] = tile[wcol + e][wrow];
-      st16(x0 + slab_off(i0 + wrow, j0 + wcol, d.l_pad), o.v);
+      st16(xu + slab_off(i0 + wrow, j0 + wcol, d.l_pad), o.v);
     }
   }
   const float total = block_sum(acc, scratch);

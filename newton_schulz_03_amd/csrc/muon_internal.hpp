@@ -58,7 +58,7 @@ struct XcdSplit {
 struct LaunchCtx {
   const MatDesc* desc;     // device copy of the descriptors
   const int32_t* prefix;   // device: NPHASE arrays of batch+1 block prefixes
-  float* partials;         // device: per reduce-block sums of squares
+  float* partials;         // device: per prepare-block sums of squares
   float* inv_norm;         // device: per matrix 1 / (||U||_F + eps)
   int32_t batch;
   int32_t max_blocks;      // matrix-core launches: most workgroups resident (0: one per tile)
