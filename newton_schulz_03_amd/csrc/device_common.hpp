@@ -113,13 +113,29 @@ __device__ __forceinline__ void* iterate(const MatDesc& d, int which) {
   return which ? d.x[1] : d.x[0];
 }
 
-// Index j with prefix[j] <= b < prefix[j+1], found by the whole block at once:
-// every thread tests a few intervals in parallel (one round of independent
-// loads) and the owner publishes j through `slot` in LDS.  Replaces a binary
-// search's chain of dependent loads at the start of every block.  Exactly one
-// interval holds b when b < prefix[batch]; empty intervals never match.
+// Index j with prefix[j] <= b < prefix[j+1] (b < prefix[batch]); exactly one
+// interval holds b, and empty intervals never match.  Up to kLocateScan
+// matrices the whole block finds it at once: every thread tests a few
+// intervals in parallel (one round of independent loads) and the owner
+// publishes j through `slot` in LDS, instead of a binary search's chain of
+// dependent loads at the start of every block.  Larger batches, where that
+// scan would cost every block `batch` loads, take the binary search (every
+// thread the same one: no LDS).  batch is uniform, so the whole block takes
+// the same branch.
+constexpr int kLocateScan = 2048;
 __device__ __forceinline__ int locate_matrix(const int32_t* prefix, int batch, int32_t b,
                                              int* slot) {
+  if (batch > kLocateScan) {
+    int lo = 0, hi = batch;  // prefix[lo] <= b < prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (prefix[mid] <= b)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return lo;
+  }
   for (int k = threadIdx.x; k < batch; k += blockDim.x)
     if (prefix[k] <= b && b < prefix[k + 1]) *slot = k;
   __syncthreads();

@@ -85,6 +85,41 @@ def test_ns_one_large_among_many_small(dtype):
     _ns_check(dtype, shapes)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_many_small_matrices(dtype):
+    """A batch of 3000 matrices of up to 40 x 40: past the size at which blocks
+    find their matrix by binary search instead of a block-wide scan, with one
+    tile per matrix in every phase.
+
+    fp32 runs the quintic for 5 steps against the oracle at 1e-4.  In bf16 the
+    5-step quintic is not held to 2e-2 on matrices this small: with only a few
+    singular directions, one that sits where the iterated polynomial is steep
+    decides the error (5e-2 measured on well-conditioned 40 x 40 inputs).  bf16
+    therefore checks maps whose error is bounded by their roundings alone,
+    through the same kernels: no iteration (X0: one rounding, 2^-9 relative),
+    and one step of (a, b, c) = (0, 1, 0) (X0 X0^T X0: the Gram and the fused
+    first-and-last product) and of (0, 0, 1) (A^2 X0: with A^2 too), a few
+    roundings each with no cancellation.
+    """
+    rng = np.random.default_rng(2024)
+    xs, hosts = [], []
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for _ in range(3000):
+        r, c = (int(v) for v in rng.integers(1, 41, size=2))
+        t = torch.from_numpy(rng.standard_normal((r, c)).astype(np.float32)).to(tdt)
+        xs.append(t.cuda())
+        hosts.append(host_f64(t))
+    runs = ([(5, oracle.QUINTIC, TOL["fp32"])] if dtype == "fp32" else
+            [(0, oracle.QUINTIC, 2.0 ** -8), (1, (0.0, 1.0, 0.0), TOL["bf16"]),
+             (1, (0.0, 0.0, 1.0), TOL["bf16"])])
+    for steps, coeffs, tol in runs:
+        outs = nsa.ns_batched(xs, steps=steps, coeffs=coeffs)
+        torch.cuda.synchronize()
+        errs = [rel_fro(host_f64(o), oracle.newton_schulz(h, steps, coeffs))
+                for o, h in zip(outs, hosts)]
+        assert max(errs) <= tol, (steps, coeffs, max(errs))
+
+
 @pytest.mark.parametrize("dtype,steps,call", [("bf16", 5, "step"), ("bf16", 1, "ns"),
                                              ("fp32", 5, "step"), ("bf16", 0, "step"),
                                              ("fp32", 0, "ns")])
