@@ -5,6 +5,9 @@ Usage:
         DIR holds the CSV output of `rocprofv3 --kernel-trace --stats`:
         a per-kernel table of calls and durations (with --muon-only, of this
         library's kernels alone).
+    python -m newton_schulz_03_amd.rocprof_summary mfma DIR --workload NAME --command "..."
+        DIR holds the CSV output of `rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16`:
+        the matrix cores' busy fraction and issued bf16 flops per kernel.
     python -m newton_schulz_03_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
             --copy-bytes N --workload NAME --command "..."
         FETCH_DIR and WRITE_DIR hold the CSV output of two runs, one with
@@ -121,6 +124,39 @@ def cmd_trace(a):
         print(f"- {short}: `{name[:160]}`")
 
 
+def counter_means(d: str):
+    """kernel short name -> {counter: mean value per dispatch}, dispatches."""
+    tot = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in csv.DictReader(open(_one_csv(d, "counter_collection.csv"))):
+        k = short_name(r["Kernel_Name"])
+        tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+    return {k: ({c: v / max(1, len(disp[k])) for c, v in tot[k].items()}, len(disp[k])) for k in tot}
+
+
+def cmd_mfma(a):
+    means = counter_means(a.dir)
+    print(f"# Matrix-core utilisation: {a.workload}\n")
+    print(f"Command (from the repository root):\n\n```\n{a.command}\n```\n")
+    print("MfmaUtil is rocprofv3's derived metric: the cycles the matrix cores were busy, "
+          "summed over all SIMDs, over the kernel's active cycles times the SIMD count.  It is "
+          "taken at whatever clock the chip ran, so it is the fraction of the matrix-core peak "
+          "at the sustained clock.  bf16 MFMA flops count every MFMA the kernel issued "
+          "(SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), the redundant lower-triangle blocks of "
+          "diagonal tiles and the identity-fragment terms included.\n")
+    print("| kernel | dispatches | MfmaUtil % | bf16 MFMA flops per dispatch |")
+    print("|---|---|---|---|")
+    rows = sorted(means.items(), key=lambda kv: -kv[1][0].get("MfmaUtil", 0.0))
+    for k, (c, n) in rows:
+        if k not in MUON_KERNELS:
+            continue
+        util = c.get("MfmaUtil")
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        print(f"| {k} | {n} | {'' if util is None else f'{util:.1f}'} | "
+              f"{'' if mops is None else f'{mops * 512:.4g}'} |")
+
+
 def cmd_traffic(a):
     fetch = counter_per_dispatch(a.fetch_dir, "FETCH_SIZE")
     write = counter_per_dispatch(a.write_dir, "WRITE_SIZE")
@@ -190,8 +226,12 @@ def main(argv=None):
     f.add_argument("--copy-bytes", type=int, required=True)
     f.add_argument("--workload", required=True)
     f.add_argument("--command", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("dir")
+    m.add_argument("--workload", required=True)
+    m.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    {"trace": cmd_trace, "traffic": cmd_traffic}[a.cmd](a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
     return 0
 
 
