@@ -83,19 +83,50 @@ struct UVec {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// k_prepare: one block per 8192-element tile of the padded wide iterate: 32 x
-// 256 for a wide matrix, 64 x 128 (short side x long side) for a tall one,
+// k_prepare: one block per tile of the padded wide iterate: kPrepWideRows x
+// 256 for a wide matrix; 64 x 128 (short side x long side) for a tall one,
 // which is read as the user's 128 x 64 tile and transposed through LDS.  Each
-// thread moves kVecs 16-byte vectors, vector v = it * 256 + threadIdx.x of the
-// tile in row-major order, so every load and store instruction of a wave
-// covers whole rows of the tile: contiguous runs of memory.  The transpose
-// holds U already rounded to T (the iterate's element type).
+// thread moves 16-byte vectors v = it * 256 + threadIdx.x of the tile in
+// row-major order, so every load and store instruction of a wave covers whole
+// rows of the tile: contiguous runs of memory.  The transpose holds U already
+// rounded to T (the iterate's element type).
 // ---------------------------------------------------------------------------
+namespace {
+
+// Loads, momentum and U for the tile's kVecs vectors per thread; returns the
+// thread's sum of squares.  The tile is read as rows of vpr vectors starting
+// at the user's (r0, c0).
+template <typename T, int kVecs>
+__device__ __forceinline__ float prepare_vectors(const MatDesc& d, const ElemParams& p, int64_t r0,
+                                                 int64_t c0, int vpr, u32x4_t* up) {
+  constexpr int V = Elt<T>::kVec;
+  UVec<T> uv[kVecs];
+#pragma unroll
+  for (int it = 0; it < kVecs; ++it) {
+    const int v = it * kThreads + threadIdx.x;
+    uv[it].load(d, p, r0 + v / vpr, c0 + (v % vpr) * V);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int it = 0; it < kVecs; ++it) {
+    const int v = it * kThreads + threadIdx.x;
+    float u[V];
+    uv[it].finish(d, p, r0 + v / vpr, c0 + (v % vpr) * V, u);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc += u[e] * u[e];
+    up[it] = f32_to_vec<T>(u);
+  }
+  return acc;
+}
+
+}  // namespace
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p) {
   constexpr int V = Elt<T>::kVec;
-  constexpr int kVecs = kPrepTile / V / kThreads;  // 4 (bf16) or 8 (fp32)
   constexpr int kTallRows = 2 * kEwTile, kTallCols = kEwTile;  // the user's tile of a tall matrix
+  constexpr int kVecsTall = kTallRows * kTallCols / V / kThreads;   // 4 (bf16) or 8 (fp32)
+  constexpr int kVecsWide = kPrepWideRows * kWideTileCols / V / kThreads;
   constexpr int kPitch = kTallCols + 4 / static_cast<int>(sizeof(T));  // one 4-byte word of padding
   __shared__ __attribute__((aligned(16))) T tile[kTallRows][kPitch];
   __shared__ float scratch[kThreads / 64];
@@ -105,58 +136,36 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
   const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, &slot));
   const MatDesc& d = c.desc[j];
   const int32_t t = b - pre[j];
-  const bool tall = d.tall != 0;
-  // tile origin in the wide iterate, and the row width (in vectors) of the tile as read
-  int64_t i0, j0;
-  int read_vpr;
-  if (!tall) {
-    const int32_t tpr = d.l_pad / kWideTileCols;
-    i0 = static_cast<int64_t>(t / tpr) * (kPrepTile / kWideTileCols);
-    j0 = static_cast<int64_t>(t % tpr) * kWideTileCols;
-    read_vpr = kWideTileCols / V;
-  } else {
-    const int32_t tpr = d.l_pad / kTallRows;
-    i0 = static_cast<int64_t>(t / tpr) * kTallCols;
-    j0 = static_cast<int64_t>(t % tpr) * kTallRows;
-    read_vpr = kTallCols / V;
-  }
-  // the user's (row, column) of each vector: wide (i0 + row, j0 + col); tall (j0 + row, i0 + col)
-  UVec<T> uv[kVecs];
-#pragma unroll
-  for (int it = 0; it < kVecs; ++it) {
-    const int v = it * kThreads + threadIdx.x;
-    const int row = v / read_vpr, col = (v % read_vpr) * V;
-    uv[it].load(d, p, (tall ? j0 : i0) + row, (tall ? i0 : j0) + col);
-  }
-  union Packed {
-    u32x4_t v;
-    T e[V];
-  } up[kVecs];  // U over each vector, rounded to T
-  float acc = 0.f;
-#pragma unroll
-  for (int it = 0; it < kVecs; ++it) {
-    const int v = it * kThreads + threadIdx.x;
-    const int row = v / read_vpr, col = (v % read_vpr) * V;
-    float u[V];
-    uv[it].finish(d, p, (tall ? j0 : i0) + row, (tall ? i0 : j0) + col, u);
-#pragma unroll
-    for (int e = 0; e < V; ++e) acc += u[e] * u[e];
-    up[it].v = f32_to_vec<T>(u);
-  }
   T* xu = static_cast<T*>(iterate(d, 0));  // the first iterate buffer, holding U
-  if (!tall) {
+  float acc;
+  if (!d.tall) {
+    // the user's rows are the iterate's: read and write the same vectors
+    const int32_t tpr = d.l_pad / kWideTileCols;
+    const int64_t i0 = static_cast<int64_t>(t / tpr) * kPrepWideRows;
+    const int64_t j0 = static_cast<int64_t>(t % tpr) * kWideTileCols;
+    constexpr int vpr = kWideTileCols / V;
+    u32x4_t up[kVecsWide];
+    acc = prepare_vectors<T, kVecsWide>(d, p, i0, j0, vpr, up);
     // V consecutive columns starting at a multiple of V stay inside one slab row
 #pragma unroll
-    for (int it = 0; it < kVecs; ++it) {
+    for (int it = 0; it < kVecsWide; ++it) {
       const int v = it * kThreads + threadIdx.x;
-      const int row = v / read_vpr, col = (v % read_vpr) * V;
-      st16(xu + slab_off(i0 + row, j0 + col, d.l_pad), up[it].v);
+      st16(xu + slab_off(i0 + v / vpr, j0 + (v % vpr) * V, d.l_pad), up[it]);
     }
   } else {
+    const int32_t tpr = d.l_pad / kTallRows;
+    const int64_t i0 = static_cast<int64_t>(t / tpr) * kTallCols;  // wide rows (short side)
+    const int64_t j0 = static_cast<int64_t>(t % tpr) * kTallRows;  // wide cols (long side)
+    constexpr int vpr = kTallCols / V;
+    union Packed {
+      u32x4_t v;
+      T e[V];
+    } up[kVecsTall];
+    acc = prepare_vectors<T, kVecsTall>(d, p, j0, i0, vpr, &up[0].v);
 #pragma unroll
-    for (int it = 0; it < kVecs; ++it) {
+    for (int it = 0; it < kVecsTall; ++it) {
       const int v = it * kThreads + threadIdx.x;
-      const int row = v / read_vpr, col = (v % read_vpr) * V;
+      const int row = v / vpr, col = (v % vpr) * V;
 #pragma unroll
       for (int e = 0; e < V; ++e) tile[row][col + e] = up[it].e[e];
     }
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
     // columns (v % wvpr) * V + 0..V-1, i.e. user rows of the tile at user column row
     constexpr int wvpr = kTallRows / V;
 #pragma unroll
-    for (int it = 0; it < kVecs; ++it) {
+    for (int it = 0; it < kVecsTall; ++it) {
       const int v = it * kThreads + threadIdx.x;
       const int wrow = v / wvpr, wcol = (v % wvpr) * V;
       Packed o;

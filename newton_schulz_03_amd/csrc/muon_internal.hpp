@@ -22,7 +22,7 @@ namespace muon {
 
 constexpr int kTile = 256;          // GEMM output tile (both sides) and padding granularity
 constexpr int kEwTile = 64;         // tile side of the finish kernel (and of prepare's tall tiles)
-constexpr int kPrepTile = 8192;     // elements per prepare block: 32 x 256 (wide) or 64 x 128 (tall)
+constexpr int kPrepWideRows = 32;   // prepare's tiles: kPrepWideRows x 256 (wide), 64 x 128 (tall)
 constexpr int kWideTileCols = 256;  // long-side width of prepare's wide tiles
 constexpr int kThreads = 256;       // threads per block, every kernel
 constexpr int kAlign = 256;         // workspace sub-buffer alignment
