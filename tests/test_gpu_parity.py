@@ -172,7 +172,10 @@ def test_ns_cubic_skips_square(dtype):
 
 @pytest.mark.parametrize("dtype,nesterov", [("bf16", False), ("bf16", True), ("fp32", False),
                                             ("fp32", True)])
-def test_step_parity(dtype, nesterov):
+@pytest.mark.parametrize("steps", [5, 1])
+def test_step_parity(dtype, nesterov, steps):
+    """Full steps against the oracle.  steps = 1: in bf16 the one product is both
+    the first (it takes the norm factor) and the last (it writes W)."""
     shapes = [(300, 700), (700, 300), (256, 768), (513, 257)]
     wl = _wl("muon", dtype, shapes, nesterov=nesterov)
     ins = device_inputs(wl)
@@ -182,16 +185,16 @@ def test_step_parity(dtype, nesterov):
     w0 = [host_f64(t) for t in w]
     g0 = [host_f64(t) for t in g]
     m0 = [host_f64(t) for t in m]
-    nsa.step_batched(w, g, m, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5)
+    nsa.step_batched(w, g, m, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=steps)
     torch.cuda.synchronize()
     # orthogonalized update of the GPU's own U, through the orthogonalize-only entry point
     us = [(gi.float() + wl.beta * mi.float()).to(gi.dtype) if nesterov else mi.clone()
           for gi, mi in zip(g, m)]
-    o_gpu = nsa.ns_batched(us, steps=5)
+    o_gpu = nsa.ns_batched(us, steps=steps)
     torch.cuda.synchronize()
     for i, (r, c) in enumerate(shapes):
         w_ref, m_ref, o_ref = oracle.muon_step(w0[i], g0[i], m0[i], lr=wl.lr, beta=wl.beta,
-                                               nesterov=nesterov, steps=5)
+                                               nesterov=nesterov, steps=steps)
         assert rel_fro(host_f64(m[i]), m_ref) <= TOL[dtype] / 4
         assert rel_fro(host_f64(o_gpu[i]), o_ref) <= TOL[dtype]
         # W' is the stored rounding of W - lr*scale*O evaluated in fp32: within one ulp of
