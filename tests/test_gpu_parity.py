@@ -86,6 +86,27 @@ def test_ns_one_large_among_many_small(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("eps", [0.0, 1.0])
+@pytest.mark.parametrize("steps", [0, 5])
+def test_eps_enters_the_normalization(dtype, eps, steps):
+    """X0 = U / (||U||_F + eps) with ||U||_F = 0.8: eps = 1 shrinks X0 to 0.44 of
+    the unit-norm iterate, so a normalization that dropped eps, or a first Gram
+    or product that took the wrong power of the factor, lands far from the
+    oracle.  With no iterations the output is X0 itself."""
+    rng = np.random.default_rng(31)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    xs = []
+    for r, c in [(300, 700), (700, 300), (256, 256)]:
+        x = rng.standard_normal((r, c))
+        xs.append(torch.from_numpy((0.8 * x / np.linalg.norm(x)).astype(np.float32)).to(tdt).cuda())
+    outs = nsa.ns_batched(xs, steps=steps, eps=eps)
+    torch.cuda.synchronize()
+    for x, o in zip(xs, outs):
+        want = oracle.newton_schulz(host_f64(x), steps, oracle.QUINTIC, eps)
+        assert rel_fro(host_f64(o), want) <= TOL[dtype], (x.shape, rel_fro(host_f64(o), want))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_many_small_matrices(dtype):
     """A batch of 3000 matrices of up to 40 x 40: past the size at which blocks
     find their matrix by binary search instead of a block-wide scan, with one
