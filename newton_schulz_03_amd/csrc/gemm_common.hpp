@@ -74,15 +74,51 @@ __device__ __forceinline__ void store4(T* p, const float* v) {
   }
 }
 
-// Upper-triangle tile (ti <= tj) number t of a T x T tile grid, row by row.
-__device__ __forceinline__ void sym_tile(int32_t t, int32_t T, int32_t& ti, int32_t& tj) {
-  int32_t i = 0;
-  while (t >= T - i) {
-    t -= T - i;
-    ++i;
+// Tile orders that keep the operand bands of concurrently running tiles few:
+// the tile rows are taken kTileGroup at a time, so a round of neighbouring
+// tiles (one XCD's 32 CUs) reads about 8 row bands and 4 column bands, not 24
+// row bands and 1 column band of a 24 x 24 grid.
+
+constexpr int32_t kTileGroup = 8;
+
+// Product tile number t of a ts x tl grid: in a group of kTileGroup tile rows,
+// rows run fastest.  With ts <= kTileGroup this is row-fastest order overall.
+__host__ __device__ __forceinline__ void prod_tile(int32_t t, int32_t ts, int32_t tl, int32_t& ti,
+                                                   int32_t& tj) {
+  const int32_t per_group = kTileGroup * tl;
+  const int32_t grp = t / per_group, first = grp * kTileGroup;
+  const int32_t g = ts - first < kTileGroup ? ts - first : kTileGroup;
+  const int32_t r = t - grp * per_group;
+  ti = first + r % g;
+  tj = r / g;
+}
+
+// Upper-triangle tile (ti <= tj) number t of a T x T tile grid.  Bands of
+// kTileGroup tile rows in order; in a band of g rows starting at row a, first
+// the g x g triangle column by column (column a + d holds rows a .. a + d),
+// then the columns right of it, g rows each.
+__host__ __device__ __forceinline__ void sym_tile(int32_t t, int32_t T, int32_t& ti, int32_t& tj) {
+  int32_t a = 0;
+  for (;;) {
+    const int32_t g = T - a < kTileGroup ? T - a : kTileGroup;
+    const int32_t tri = g * (g + 1) / 2;
+    const int32_t band = tri + g * (T - a - g);
+    if (t < band) {
+      if (t < tri) {
+        int32_t d = 0;
+        while ((d + 1) * (d + 2) / 2 <= t) ++d;
+        ti = a + (t - d * (d + 1) / 2);
+        tj = a + d;
+      } else {
+        const int32_t r = t - tri;
+        ti = a + r % g;
+        tj = a + g + r / g;
+      }
+      return;
+    }
+    t -= band;
+    a += kTileGroup;
   }
-  ti = i;
-  tj = i + t;
 }
 
 struct TileRef {
@@ -130,8 +166,7 @@ __device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int32_t b, in
   const int32_t t = b - pre[j];
   const int32_t ts = r.d.s_pad / kTile;
   if constexpr (MODE == GM_PROD) {
-    r.ti = t % ts;  // tile row along the short side, fastest: neighbours share X columns
-    r.tj = t / ts;
+    prod_tile(t, ts, r.d.l_pad / kTile, r.ti, r.tj);
   } else {
     sym_tile(t, ts, r.ti, r.tj);
   }

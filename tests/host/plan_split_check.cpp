@@ -8,6 +8,7 @@
 //   - split_tile (the function the kernels call) maps the grid's workgroups
 //     onto every tile exactly once, the rest to -1;
 //   - every XCD's range holds at most 1/8 of the launch's work plus one tile.
+//   - the tile orders (prod_tile, sym_tile) take every tile of a grid once.
 // Prints "OK <plans>" and exits 0, or names the first failure and exits 1.
 #include "muon_abi.hip"
 
@@ -110,6 +111,31 @@ int main() {
     check_split(pl.split_poly, sym, k_short, trial);
     check_split(pl.split_prod, prod, k_short, trial);
     ++plans;
+  }
+  // the tile orders: every tile of a grid exactly once
+  for (int32_t ts = 1; ts <= 40; ++ts) {
+    for (int32_t tl = ts; tl <= ts + 9; ++tl) {
+      std::vector<int> seen(static_cast<size_t>(ts) * tl, 0);
+      for (int32_t t = 0; t < ts * tl; ++t) {
+        int32_t ti = -1, tj = -1;
+        prod_tile(t, ts, tl, ti, tj);
+        const bool ok = ti >= 0 && ti < ts && tj >= 0 && tj < tl;
+        expect(ok, "prod_tile out of the grid", ts);
+        if (ok) seen[static_cast<size_t>(ti) * tl + tj]++;
+      }
+      for (int v : seen) expect(v == 1, "prod_tile does not take every tile once", ts);
+    }
+    std::vector<int> seen(static_cast<size_t>(ts) * ts, 0);
+    for (int32_t t = 0; t < ts * (ts + 1) / 2; ++t) {
+      int32_t ti = -1, tj = -1;
+      sym_tile(t, ts, ti, tj);
+      const bool ok = ti >= 0 && ti <= tj && tj < ts;
+      expect(ok, "sym_tile outside the upper triangle", ts);
+      if (ok) seen[static_cast<size_t>(ti) * ts + tj]++;
+    }
+    for (int32_t i = 0; i < ts; ++i)
+      for (int32_t jj = i; jj < ts; ++jj)
+        expect(seen[static_cast<size_t>(i) * ts + jj] == 1, "sym_tile does not take every tile once", ts);
   }
   // a uniform batch keeps equal ranges and one workgroup per tile
   {
