@@ -68,15 +68,17 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, int32_t voff, i32x4
                : "memory", "m0");
 }
 
-// One operand's stream of 256 x 32 tiles into the LDS ring.  In the slab layout
-// (slab_off in device_common.hpp) a K-major tile is one contiguous 16 KiB slab;
-// the product's MN-major tile (32 rows of X x 256 columns) is 8 contiguous
-// 2 KiB pieces, one per slab.
-struct Stream {
+// One operand's stream of 256 x 32 (or, for the wide product's X, 32 x 384)
+// tiles into the LDS ring, N 16-byte loads per thread and slice.  In the slab
+// layout (slab_off in device_common.hpp) a K-major tile is one contiguous
+// 16 KiB slab; the product's MN-major tile (32 rows of X x 64 N columns) is 2 N
+// contiguous 2 KiB pieces, one per slab.
+template <int N>
+struct StreamT {
   const char* base;      // byte address at k-slice 0 (uniform)
   int64_t band_stride;   // MN-major: bytes between bands of 256 rows
   int32_t mn;            // 1: MN-major, 0: K-major
-  int32_t voff[LPO];     // per-lane byte offsets, one per load instruction
+  int32_t voff[N];       // per-lane byte offsets, one per load instruction
   int32_t lds;           // LDS byte offset of this wave's first 1 KiB block, within the operand
 
   // Buffer resource for k-slice ks: base, stride 0, num_records (bytes), raw dword access.
@@ -88,7 +90,7 @@ struct Stream {
     i32x4_t r;
     r[0] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(b & 0xffffffffu));
     r[1] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>((b >> 32) & 0xffffu));
-    r[2] = mn ? 7 * OPB + 32 * KROW : OPB;  // exactly the bytes this slice reads
+    r[2] = mn ? (2 * N - 1) * OPB + 32 * KROW : OPB;  // exactly the bytes this slice reads
     r[3] = 0x00020000;
     return r;
   }
@@ -98,10 +100,11 @@ struct Stream {
   __device__ __forceinline__ void issue(int ks, uint32_t stage_op_lds) const {
     const i32x4_t r = rsrc(ks);
 #pragma unroll
-    for (int u = 0; u < LPO; ++u)
+    for (int u = 0; u < N; ++u)
       lds_dma16(__builtin_amdgcn_readfirstlane(stage_op_lds + lds + u * 1024), voff[u], r);
   }
 };
+using Stream = StreamT<LPO>;
 
 // Rows [256 band, 256 band + 256) of a slab-layout matrix with `ncols` columns.
 // LDS: 256 rows of 64 bytes, chunk c of row r kept at c ^ kkey(r).
@@ -121,24 +124,25 @@ __device__ __forceinline__ Stream kmajor_stream(const uint16_t* m, int64_t band,
   return s;
 }
 
-// Columns [256 tj, 256 tj + 256) of a slab-layout matrix (all its rows, 32 per
-// k-slice).  LDS: 8 pieces (one per slab) of 32 rows x 64 bytes, chunk c of row
-// r kept at c ^ (2 ((r >> 1) & 1)).
-__device__ __forceinline__ Stream mnmajor_stream(const uint16_t* m, int64_t tj, int64_t ncols,
-                                                 int wave, int lane) {
-  Stream s;
+// Columns [W tj, W tj + W) of a slab-layout matrix, W = 64 N (all its rows, 32
+// per k-slice).  LDS: 2 N pieces (one per slab) of 32 rows x 64 bytes, chunk c
+// of row r kept at c ^ (2 ((r >> 1) & 1)).
+template <int N>
+__device__ __forceinline__ StreamT<N> mnmajor_stream(const uint16_t* m, int64_t tj, int64_t ncols,
+                                                     int wave, int lane) {
+  StreamT<N> s;
   const int64_t slabs_per_band = ncols / kSlabCols;
-  s.base = reinterpret_cast<const char*>(m + 8 * tj * (kSlabRows * kSlabCols));
+  s.base = reinterpret_cast<const char*>(m + 2 * N * tj * (kSlabRows * kSlabCols));
   s.band_stride = slabs_per_band * OPB;
   s.mn = 1;
 #pragma unroll
-  for (int u = 0; u < LPO; ++u) {
-    const int blk = LPO * wave + u;  // 1 KiB block: slab piece blk / 2, rows 16 (blk % 2) ..
+  for (int u = 0; u < N; ++u) {
+    const int blk = N * wave + u;  // 1 KiB block: slab piece blk / 2, rows 16 (blk % 2) ..
     const int row = 16 * (blk & 1) + (lane >> 2);
     const int c = (lane & 3) ^ (2 * ((row >> 1) & 1));
     s.voff[u] = (blk >> 1) * OPB + row * KROW + c * 16;
   }
-  s.lds = LPO * wave * 1024;
+  s.lds = N * wave * 1024;
   return s;
 }
 
@@ -411,7 +415,7 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   } else {
     K = s_pad;
     const uint16_t* Q = static_cast<const uint16_t*>(g.use_poly ? d.poly : d.gram);
-    sp = mnmajor_stream(Xc, tr.tj, l_pad, wave, lane);
+    sp = mnmajor_stream<LPO>(Xc, tr.tj, l_pad, wave, lane);
     sq = kmajor_stream(Q, tr.ti, s_pad, wave, lane);
   }
   const int nk = static_cast<int>(K / BK);
@@ -596,6 +600,289 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
     store_tile_lds<MODE>(acc, tr, g, nf, smem, wave, lane);
 }
 
+// ---------------------------------------------------------------------------
+// Wide product tiles: 256 rows of B (q) x 384 columns of X (p).
+//
+// Per K slice such a tile streams 40 KiB for 6.3 MFLOP, where a 256 x 256 tile
+// streams 32 KiB for 4.2 MFLOP: 17% fewer operand bytes per flop, and the
+// per-slice barrier and waits are spread over 1.5x the matrix-core work.  The
+// four waves keep a 2 x 2 grid of 192 (p) x 128 (q) blocks, 24 accumulator
+// blocks of 32 x 32 and 384 fp32 registers per lane.  The compiler places MFMA
+// accumulators in AGPRs only (256 per lane), so p-blocks 0..3 stay ordinary
+// MFMAs on AGPRs (acc) and p-blocks 4..5 are inline VGPR-form MFMAs (accv).
+// The main loop needs fewer than 100 other VGPRs.
+//   Hazards of the inline MFMAs: their A/B operands come from LDS reads, which
+//   the compiler guards with lgkmcnt waits like any other use; the MFMAs into
+//   one block are at least 6 MFMAs apart; the zeroing of accv and the
+//   epilogue's reads of it are separated from the MFMAs by mfma_guard.
+// LDS: a 4-stage ring of 40 KiB stages (the X slice, 24 KiB, then the B slice),
+// all 160 KiB of the CU.  The tile is stored through LDS in two halves of
+// 256 x 192.  Every output element takes the same MFMAs in the same order as
+// in the 256 x 256 kernel, so the results are bit-identical.
+constexpr int LPW = kTileW * KROW / (kThreads * 16);  // loads per thread and slice, X slice (6)
+constexpr int OPBW = kTileW * KROW;                   // 24 KiB: the X slice of a stage
+constexpr int STAGEW = OPBW + OPB;                    // 40 KiB
+constexpr int LDSW = NST * STAGEW;                    // 160 KiB
+constexpr int WROW = kTileW;                          // bytes of a staged half-tile row (192 bf16)
+static_assert(LPW == 6 && LDSW == 163840, "wide tile geometry");
+static_assert(kTile * WROW <= LDSW, "a staged half tile fits in the ring");
+
+// d += a b on VGPR accumulators.
+__device__ __forceinline__ void mfma_v(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// Wait states between the inline MFMAs and any other write or read of their
+// accumulators (the compiler does not look inside inline assembly).
+__device__ __forceinline__ void mfma_guard(f32x16_t (&v)[2][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]), "+v"(v[1][0]),
+                 "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]));
+}
+
+// Tile number b of a wide product launch -> (matrix, tile), as decode_tile.
+__device__ __forceinline__ TileRef decode_wide(const LaunchCtx& c, int32_t b, int* slot) {
+  const int32_t* pre = c.prefix + PH_PRODW * (c.batch + 1);
+  const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
+  TileRef r;
+  r.d = c.desc[j];
+  r.mat = j;
+  prod_tile(b - pre[j], r.d.s_pad / kTile, r.d.l_pad / kTileW, r.ti, r.tj);
+  return r;
+}
+
+// Stores X'[ti*256 + q][tj*384 + p] = nf * acc (bf16) into the other iterate
+// buffer, through LDS in halves h = 0, 1.  Half h holds p-blocks 3h .. 3h+2 of
+// every wave: columns tj*384 + 192 wm + 96 h + (0 .. 95), wm = 0, 1.  A staged
+// half is 256 rows of 192 values (24 chunks of 16 bytes); chunk c of row q is
+// kept at c ^ ((q >> 1) & 7), so that both the staging writes and the reads
+// below spread over all banks.  It goes out in units of 16 rows x one
+// 32-column slab, 1 KiB of consecutive bytes in the slab layout, one unit per
+// wave instruction.
+__device__ __forceinline__ void store_wide(const f32x16_t (&acc)[4][4], const f32x16_t (&accv)[2][4],
+                                           const TileRef& tr, const GemmArgs& g, float nf,
+                                           char* smem, int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  uint16_t* __restrict__ dst = static_cast<uint16_t*>(iterate(tr.d, g.cur ^ 1));
+  const int64_t ld = tr.d.l_pad;
+  const int64_t r0 = static_cast<int64_t>(tr.ti) * kTile;
+  const int64_t cw = static_cast<int64_t>(tr.tj) * kTileW;
+  // p-block 3h + ml of this wave (its four q-blocks) into the staged half
+  auto stage_mi = [&](const f32x16_t (&a)[4], int ml) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int q = wn * 128 + ni * 32 + lr;
+        const int c = 12 * wm + 4 * ml + gg;
+        u32x2_t w;
+        w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 0])) |
+               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 1])) << 16);
+        w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 2])) |
+               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 3])) << 16);
+        *reinterpret_cast<u32x2_t*>(smem + q * WROW + ((c ^ ((q >> 1) & 7)) << 4) + 8 * lh) = w;
+      }
+  };
+  auto store_half = [&](int h) {
+#pragma unroll 4
+    for (int v = 0; v < 24; ++v) {
+      const int unit = 24 * wave + v;  // slab gs = unit % 6 of the half, rows 16 (unit / 6) ..
+      const int gs = unit % 6, rg = unit / 6;
+      const int q = 16 * rg + (lane & 15);
+      const int c = 4 * gs + (lane >> 4);
+      const u32x4_t val =
+          *reinterpret_cast<const u32x4_t*>(smem + q * WROW + ((c ^ ((q >> 1) & 7)) << 4));
+      const int64_t col = cw + 192 * (gs / 3) + 96 * h + 32 * (gs % 3) + 8 * (lane >> 4);
+      st16(dst + slab_off(r0 + q, col, ld), val);
+    }
+  };
+  stage_mi(acc[0], 0);
+  stage_mi(acc[1], 1);
+  stage_mi(acc[2], 2);
+  __syncthreads();
+  store_half(0);
+  __syncthreads();  // every wave has read half 0 before half 1 overwrites it
+  stage_mi(acc[3], 0);
+  stage_mi(accv[0], 1);
+  stage_mi(accv[1], 2);
+  __syncthreads();
+  store_half(1);
+}
+
+// One wide product tile (tile number t of the launch): X' = a X + Q X into the
+// other iterate buffer, scaled by the norm factor in the FIRST product.  The
+// pipeline is gemm_tile's (ring, waits, fragment order, fused a X term) with
+// six p-blocks per wave instead of four.
+template <bool FIRST>
+__device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArgs& g, int32_t t,
+                                               char* smem, int* slot) {
+  const TileRef tr = decode_wide(c, t, slot);
+  const MatDesc& d = tr.d;
+  const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
+  const uint16_t* Xc = static_cast<const uint16_t*>(iterate(d, g.cur));
+  const uint16_t* Q = static_cast<const uint16_t*>(g.use_poly ? d.poly : d.gram);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+
+  const StreamT<LPW> sp = mnmajor_stream<LPW>(Xc, tr.tj, l_pad, wave, lane);
+  const Stream sq = kmajor_stream(Q, tr.ti, s_pad, wave, lane);
+  const int nk = static_cast<int>(s_pad / BK);
+
+  // Fragment offsets within a stage, as in gemm_tile; the X slice comes first.
+  int32_t qoff[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int sw = ((2 * sub + lh) ^ kkey(lr)) << 4;
+    qoff[sub] = OPBW + (wn * 128 + lr) * KROW + sw;
+  }
+  int32_t moff0;
+  {
+    const int gq = lane >> 4, r = (lane >> 2) & 3, qq = lane & 3;
+    const int cc = 2 * (gq & 1) + (qq >> 1);
+    moff0 = 6 * wm * (32 * KROW) + (8 * (gq >> 1) + r) * KROW +
+            ((cc ^ (2 * ((r >> 1) & 1))) << 4) + 8 * (qq & 1);
+  }
+
+  struct FragsW {
+    u32x4_t p[6];
+    u32x4_t q[4];
+  };
+  // Reads in the order the MFMAs consume them: P[0] (two transposed halves),
+  // Q[0..3], then P[1..5].
+  constexpr int NREADW = 16;
+  auto read_op = [&](FragsW& f, const char* stage, int sub, int i) {
+    if (i >= 2 && i < 6) {
+      f.q[i - 2] = lds16(stage + qoff[sub] + (i - 2) * 32 * KROW);
+    } else {
+      const int mi = i < 2 ? 0 : 1 + (i - 6) / 2, h = i < 2 ? i : (i - 6) % 2;
+      const char* base = stage + moff0 + mi * (32 * KROW) + (16 * sub + 4 * h) * KROW;
+      const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(base));
+      const u32x2_t u = __builtin_bit_cast(u32x2_t, v);
+      f.p[mi][2 * h] = u[0];
+      f.p[mi][2 * h + 1] = u[1];
+    }
+  };
+
+  f32x16_t acc[4][4];
+  zero_acc(acc);
+  f32x16_t accv[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) accv[mi][ni][e] = 0.f;
+  mfma_guard(accv);
+
+  auto mma = [&](int mi, int ni, const u32x4_t& a, const u32x4_t& b) {
+    if (mi < 4)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), acc[mi][ni], 0, 0, 0);
+    else
+      mfma_v(accv[mi - 4][ni], a, b);
+  };
+  auto mfma_op = [&](const FragsW& f, int i) { mma(i >> 2, i & 3, f.p[i >> 2], f.q[i & 3]); };
+
+  // The a X term, as in gemm_tile: the X fragments times a scaled identity, in
+  // hi and lo bf16 parts (all hi parts first, so that no two MFMAs into one
+  // block follow each other).
+  const __bf16 s_hi = static_cast<__bf16>(g.init_scale);
+  const __bf16 s_lo = static_cast<__bf16>(g.init_scale - static_cast<float>(s_hi));
+  auto ident = [&](int h, __bf16 v) {
+    bf16x8_t r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = lr == 16 * h + 8 * lh + e ? v : static_cast<__bf16>(0.f);
+    return r;
+  };
+  // The identity fragments are built by VALU instructions: the guard puts wait
+  // states between them and the inline MFMAs that read them, and the fences
+  // keep the twelve MFMAs in this order.
+  auto term_op = [&](const FragsW& f, int h, auto R) {
+    constexpr int r = decltype(R)::value;
+    if constexpr (r >= 0) {
+      u32x4_t id[2] = {__builtin_bit_cast(u32x4_t, ident(h, s_hi)),
+                       __builtin_bit_cast(u32x4_t, ident(h, s_lo))};
+      asm volatile("s_nop 4" : "+v"(id[0]), "+v"(id[1]));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int part = 0; part < 2; ++part)
+#pragma unroll
+        for (int x = 0; x < 6; ++x) {
+          mma(x, r, f.p[x], id[part]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  };
+
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)smem));
+
+  // Prologue: slices 0..NST-2 requested, slice 0 awaited (past the end: clamped).
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) {
+    const int ks = s < nk ? s : nk - 1;
+    sp.issue(ks, ring + s * STAGEW);
+    sq.issue(ks, ring + s * STAGEW + OPBW);
+  }
+  wait_vm<(NST - 2) * (LPW + LPO)>();
+  __syncthreads();
+
+  FragsW f0, f1;
+#pragma unroll
+  for (int i = 0; i < NREADW; ++i) read_op(f0, smem, 0, i);
+
+  // One K slice: 24 steps of {memory op(s), one MFMA} per half; the X-slice
+  // loads of stage kt+NST-1 go out in the first half (one every 4 MFMAs), the
+  // B-slice loads in the second (one every 6).
+  auto slice = [&](int kt, auto R) {
+    const char* stage = smem + (kt & (NST - 1)) * STAGEW;
+    const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
+    const uint32_t fill = ring + ((kt + NST - 1) & (NST - 1)) * STAGEW;
+    const i32x4_t rp = sp.rsrc(ks);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      if ((i & 3) == 0) sp.issue_one(rp, fill, i >> 2);
+      if (i < NREADW) read_op(f1, stage, 1, i);
+      mfma_op(f0, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    term_op(f0, 0, R);
+    __builtin_amdgcn_sched_barrier(0);
+    // slice kt+1 has landed once only slice kt+2 and the X half of kt+NST-1 remain
+    wait_vm<(NST - 3) * (LPW + LPO) + LPW>();
+    wait_lgkm0();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const i32x4_t rq = sq.rsrc(ks);
+    const char* next = smem + ((kt + 1) & (NST - 1)) * STAGEW;
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      if (i % 6 == 0) sq.issue_one(rq, fill + OPBW, i / 6);
+      if (i < NREADW) read_op(f0, next, 0, i);
+      mfma_op(f1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    term_op(f1, 1, R);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using NoTerm = std::integral_constant<int, -1>;
+  const int rel0 = __builtin_amdgcn_readfirstlane(8 * tr.ti + 4 * wn);
+  for (int kt = 0; kt < rel0; ++kt) slice(kt, NoTerm{});
+  slice(rel0 + 0, std::integral_constant<int, 0>{});
+  slice(rel0 + 1, std::integral_constant<int, 1>{});
+  slice(rel0 + 2, std::integral_constant<int, 2>{});
+  slice(rel0 + 3, std::integral_constant<int, 3>{});
+  for (int kt = rel0 + 4; kt < nk; ++kt) slice(kt, NoTerm{});
+  wait_vm<0>();
+  __syncthreads();
+  mfma_guard(accv);
+  const float nf = FIRST ? c.inv_norm[tr.mat] : 1.f;
+  store_wide(acc, accv, tr, g, nf, smem, wave, lane);
+}
+
 // One block per CU, one tile per block, taken by split_tile: the XCDs get
 // ranges of equal work.  LOOP (a CU budget: fewer workgroups than tiles): a
 // block takes tiles blockIdx.x, blockIdx.x + gridDim.x, ..., renumbered so that
@@ -628,6 +915,17 @@ void launch_one(const LaunchCtx& c, int32_t nblocks, bool loop, const GemmArgs& 
                        c.stream, c, g);
 }
 
+// Wide product tiles, one per workgroup (split_tile).  The matrix lookup's LDS
+// slot sits in the last ring stage, which the prologue leaves unfilled: every
+// wave has read it before the first slice refills that stage.
+template <bool FIRST>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16_wide(LaunchCtx c, GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDSW];
+  const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
+  if (t < 0) return;  // the whole block: t depends on blockIdx.x only
+  gemm_tile_wide<FIRST>(c, g, t, smem, reinterpret_cast<int*>(smem + (NST - 1) * STAGEW));
+}
+
 template <bool FINAL>
 void launch_prod_bf16(const LaunchCtx& c, int32_t nblocks, bool loop, const GemmArgs& g) {
   if (g.first)
@@ -651,6 +949,18 @@ hipError_t launch_gemm_bf16(int mode, const LaunchCtx& c, int32_t nblocks, bool 
         launch_prod_bf16<false>(c, nblocks, loop, g);
       break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_prod_wide(const LaunchCtx& c, const XcdSplit& sp, int32_t cur, float a,
+                            bool use_poly, bool first) {
+  const int32_t ntiles = sp.lo[kXcd];
+  if (ntiles <= 0) return hipSuccess;
+  const GemmArgs g{cur, a, 1.f, use_poly ? 1 : 0, FIN_NONE, 0.f, first ? 1 : 0, ntiles, sp};
+  if (first)
+    hipLaunchKernelGGL((k_gemm_bf16_wide<true>), dim3(sp.grid), dim3(kThreads), 0, c.stream, c, g);
+  else
+    hipLaunchKernelGGL((k_gemm_bf16_wide<false>), dim3(sp.grid), dim3(kThreads), 0, c.stream, c, g);
   return hipGetLastError();
 }
 

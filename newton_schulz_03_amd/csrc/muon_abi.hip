@@ -41,8 +41,12 @@ struct Plan {
   std::vector<MatDesc> desc;        // workspace pointers filled in by bind()
   std::vector<size_t> mat_off;      // byte offset of matrix i's buffers
   std::vector<int32_t> prefix;      // NPHASE x (batch + 1)
-  int32_t totals[NPHASE] = {0, 0, 0, 0};
+  int32_t totals[NPHASE] = {0, 0, 0, 0, 0};
   XcdSplit split_gram{}, split_poly{}, split_prod{};  // matrix-core launches over the XCDs
+  // Wide product tiles (256 x kTileW): every matrix's padded long side is a
+  // multiple of kTileW.  Then the products that store the iterate use them.
+  bool wide_prod = false;
+  XcdSplit split_prodw{};
   size_t table_bytes = 0;
   size_t inv_off = 0;
   size_t partials_off = 0;
@@ -98,10 +102,12 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
   pl.desc.assign(batch, MatDesc{});
   pl.mat_off.assign(batch, 0);
   pl.prefix.assign(static_cast<size_t>(NPHASE) * (batch + 1), 0);
-  int64_t tot[NPHASE] = {0, 0, 0, 0};
+  int64_t tot[NPHASE] = {0, 0, 0, 0, 0};
   // per matrix: symmetric and product tiles; K slices of the Gram (long side)
   // and of A^2 and the product (short side)
-  std::vector<int64_t> sym_cnt(batch), prod_cnt(batch), k_long(batch), k_short(batch);
+  std::vector<int64_t> sym_cnt(batch), prod_cnt(batch), prodw_cnt(batch), k_long(batch),
+      k_short(batch);
+  bool all_wide = batch > 0;
   for (int32_t i = 0; i < batch; ++i) {
     const int64_t r = rows[i], c = cols[i];
     if (r <= 0 || c <= 0)
@@ -128,9 +134,12 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
         ts * (ts + 1) / 2,                                                   // PH_SYM
         ts * tl,                                                             // PH_PROD
         cdiv(r, kEwTile) * cdiv(c, kEwTile),                                 // PH_FINISH
+        d.l_pad % kTileW == 0 ? ts * (d.l_pad / kTileW) : 0,                 // PH_PRODW
     };
     sym_cnt[i] = cnt[PH_SYM];
     prod_cnt[i] = cnt[PH_PROD];
+    prodw_cnt[i] = cnt[PH_PRODW];
+    all_wide = all_wide && d.l_pad % kTileW == 0;
     k_long[i] = d.l_pad / 32;
     k_short[i] = d.s_pad / 32;
     for (int ph = 0; ph < NPHASE; ++ph) {
@@ -148,6 +157,8 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
   if ((st = make_split(sym_cnt, k_long, pl.split_gram)) != MUON_OK) return st;
   if ((st = make_split(sym_cnt, k_short, pl.split_poly)) != MUON_OK) return st;
   if ((st = make_split(prod_cnt, k_short, pl.split_prod)) != MUON_OK) return st;
+  pl.wide_prod = all_wide && pl.bf16;
+  if (pl.wide_prod && (st = make_split(prodw_cnt, k_short, pl.split_prodw)) != MUON_OK) return st;
   size_t off = 0;
   off += align_up(sizeof(MatDesc) * batch, kAlign);
   off += align_up(sizeof(int32_t) * pl.prefix.size(), kAlign);
@@ -408,9 +419,15 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
     {
       TimedLaunch t(last ? MUON_K_PROD_FINISH : k == 0 ? MUON_K_PROD_FIRST : MUON_K_PROD, stream);
       const int32_t fin = !last ? FIN_NONE : ep.mode == MODE_STEP ? FIN_STEP : FIN_NS;
-      if ((e = launch_prod(c, pl.split_prod, pl.bf16, cur, ns.a, use_poly, k == 0, fin,
-                           ep.lr)) != hipSuccess)
+      // wide tiles for the products that store the iterate, unless a CU budget
+      // asks for the looping launches (256-wide tiles only)
+      if (pl.wide_prod && fin == FIN_NONE && ns.cu_budget == 0) {
+        if ((e = launch_prod_wide(c, pl.split_prodw, cur, ns.a, use_poly, k == 0)) != hipSuccess)
+          return hip_fail(e, "launch product (wide tiles)");
+      } else if ((e = launch_prod(c, pl.split_prod, pl.bf16, cur, ns.a, use_poly, k == 0, fin,
+                                  ep.lr)) != hipSuccess) {
         return hip_fail(e, "launch product");
+      }
       t.done();
     }
     cur ^= 1;

@@ -21,6 +21,7 @@
 namespace muon {
 
 constexpr int kTile = 256;          // GEMM output tile (both sides) and padding granularity
+constexpr int kTileW = 384;         // columns of X in a wide product tile (256 rows of B x 384)
 constexpr int kEwTile = 64;         // tile side of the finish kernel (and of prepare's tall tiles)
 constexpr int kPrepWideRows = 32;   // prepare's tiles: kPrepWideRows x 256 (wide), 64 x 128 (tall)
 constexpr int kWideTileCols = 256;  // long-side width of prepare's wide tiles
@@ -28,7 +29,7 @@ constexpr int kThreads = 256;       // threads per block, every kernel
 constexpr int kAlign = 256;         // workspace sub-buffer alignment
 constexpr int kXcd = 8;             // XCDs of the chip: workgroup b runs on XCD b % 8
 
-enum Phase : int { PH_PREPARE = 0, PH_SYM = 1, PH_PROD = 2, PH_FINISH = 3, NPHASE = 4 };
+enum Phase : int { PH_PREPARE = 0, PH_SYM = 1, PH_PROD = 2, PH_FINISH = 3, PH_PRODW = 4, NPHASE = 5 };
 enum Mode : int { MODE_NS = 0, MODE_STEP = 1 };
 
 struct MatDesc {
@@ -123,5 +124,11 @@ hipError_t launch_poly(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, flo
 // the user's matrix (W - lr * scale * X', or the output) instead of X[next].
 hipError_t launch_prod(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int32_t cur,
                        float a, bool use_poly, bool first, int32_t finish = 0, float lr = 0.f);
+// The same product into X[next], bf16 only, in tiles of 256 rows x kTileW
+// columns (the PH_PRODW tiles that `sp` splits; every l_pad a multiple of
+// kTileW).  Bit-identical to launch_prod: each output element accumulates the
+// same MFMAs in the same order.
+hipError_t launch_prod_wide(const LaunchCtx& c, const XcdSplit& sp, int32_t cur, float a,
+                            bool use_poly, bool first);
 
 }  // namespace muon

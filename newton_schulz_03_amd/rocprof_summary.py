@@ -35,9 +35,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_common.hpp",
                   "csrc/muon_internal.hpp")
 
+# The wide-tile products (256 x 384 tiles) take the labels of the products they
+# replace: a call uses one kind or the other for all of its middle products.
 SHORT_NAMES = (("k_gemm_bf16<0,false,false,false>", "gram"), ("k_gemm_bf16<1,false,false,false>", "poly"),
                ("k_gemm_bf16<2,false,false,false>", "prod"),
                ("k_gemm_bf16<2,false,false,true>", "prod_first"),
+               ("k_gemm_bf16_wide<false>", "prod"), ("k_gemm_bf16_wide<true>", "prod_first"),
                ("k_gemm_bf16<2,true,false,false>", "prod_finish"),
                ("k_gemm_bf16<2,true,false,true>", "prod_finish_first"),
                ("k_gemm_bf16<0,false,true,false>", "gram_budget"),

@@ -9,6 +9,8 @@
 //     onto every tile exactly once, the rest to -1;
 //   - every XCD's range holds at most 1/8 of the launch's work plus one tile.
 //   - the tile orders (prod_tile, sym_tile) take every tile of a grid once.
+//   - the wide product tiles (256 x kTileW) are planned exactly when every
+//     padded long side is a multiple of kTileW, in bf16, and split the same way.
 // Prints "OK <plans>" and exits 0, or names the first failure and exits 1.
 #include "muon_abi.hip"
 
@@ -26,6 +28,9 @@ hipError_t launch_poly(const LaunchCtx&, const XcdSplit&, bool, float, float) {
 }
 hipError_t launch_prod(const LaunchCtx&, const XcdSplit&, bool, int32_t, float, bool, bool,
                        int32_t, float) {
+  return hipSuccess;
+}
+hipError_t launch_prod_wide(const LaunchCtx&, const XcdSplit&, int32_t, float, bool, bool) {
   return hipSuccess;
 }
 hipError_t launch_adamw(const AdamCtx&, int32_t, bool, const AdamParams&) { return hipSuccess; }
@@ -86,12 +91,19 @@ int main() {
   std::mt19937 rng(12345);
   const int64_t dims[] = {1, 7, 255, 256, 257, 512, 1000, 1024, 2048, 4095, 6144, 8192};
   int plans = 0;
-  for (int trial = 0; trial < 600; ++trial) {
+  // long sides whose padding is a multiple of kTileW, for batches that take wide tiles
+  const int64_t wide_dims[] = {700, 768, 1500, 1536, 2304, 3000, 6144, 6100};
+  for (int trial = 0; trial < 900; ++trial) {
     const int batch = 1 + static_cast<int>(rng() % (trial < 500 ? 24 : 300));
     std::vector<int64_t> r(batch), c(batch);
     for (int i = 0; i < batch; ++i) {
       r[i] = dims[rng() % 12];
       c[i] = dims[rng() % 12];
+      if (trial >= 600) {  // a wide-tile batch: long side from wide_dims, short side below it
+        const int64_t l = wide_dims[rng() % 8], sh = 1 + static_cast<int64_t>(rng() % l);
+        r[i] = (rng() & 1) ? l : sh;
+        c[i] = r[i] == l ? sh : l;
+      }
     }
     Plan pl;
     const int32_t dtype = (trial & 1) ? MUON_FP32 : MUON_BF16;
@@ -99,17 +111,23 @@ int main() {
       expect(false, "make_plan failed", trial);
       continue;
     }
-    std::vector<int64_t> sym(batch), prod(batch), k_long(batch), k_short(batch);
+    std::vector<int64_t> sym(batch), prod(batch), prodw(batch), k_long(batch), k_short(batch);
+    bool all_wide = true;
     for (int i = 0; i < batch; ++i) {
       const int64_t ts = pl.desc[i].s_pad / kTile, tl = pl.desc[i].l_pad / kTile;
       sym[i] = ts * (ts + 1) / 2;
       prod[i] = ts * tl;
+      prodw[i] = ts * (pl.desc[i].l_pad / kTileW);
+      all_wide = all_wide && pl.desc[i].l_pad % kTileW == 0;
       k_long[i] = pl.desc[i].l_pad / 32;
       k_short[i] = pl.desc[i].s_pad / 32;
     }
     check_split(pl.split_gram, sym, k_long, trial);
     check_split(pl.split_poly, sym, k_short, trial);
     check_split(pl.split_prod, prod, k_short, trial);
+    expect(pl.wide_prod == (all_wide && dtype == MUON_BF16), "wide tiles planned wrongly", trial);
+    expect(trial < 600 || dtype != MUON_BF16 || pl.wide_prod, "wide-tile batch not wide", trial);
+    if (pl.wide_prod) check_split(pl.split_prodw, prodw, k_short, trial);
     ++plans;
   }
   // the tile orders: every tile of a grid exactly once
@@ -144,6 +162,9 @@ int main() {
     expect(make_plan(96, r.data(), c.data(), MUON_BF16, pl) == MUON_OK, "uniform plan", -1);
     expect(pl.split_prod.grid == 18432 && pl.split_gram.grid == 3456, "uniform grid", -1);
     for (int x = 0; x <= kXcd; ++x) expect(pl.split_prod.lo[x] == 2304 * x, "uniform ranges", -1);
+    expect(pl.wide_prod && pl.split_prodw.grid == 12288, "uniform wide grid", -1);
+    for (int x = 0; x <= kXcd; ++x)
+      expect(pl.split_prodw.lo[x] == 1536 * x, "uniform wide ranges", -1);
   }
   // an empty batch launches nothing
   {
