@@ -436,6 +436,39 @@ def test_rank_deficient_inputs(dtype):
         assert np.all(oh[zr, :] == 0) and np.all(oh[:, zc] == 0)
 
 
+@pytest.mark.parametrize("case", ["many", "cubic"])
+def test_wide_product_tiles_match_square_tiles(case):
+    """The first and middle products run in 256 x 384 tiles when every padded
+    long side is a multiple of 384; a CU budget (here larger than any grid)
+    selects the 256 x 256 kernel instead.  Both accumulate every element with
+    the same MFMAs in the same order, so the outputs agree bit for bit.
+    many: 2100 matrices, past the batch size at which blocks find their matrix
+    by binary search; cubic: (1.5, -0.5, 0), where the product reads A itself."""
+    rng = np.random.default_rng(99)
+    if case == "many":
+        shapes = []
+        for _ in range(2100):
+            s, l = int(rng.integers(1, 41)), int(rng.integers(513, 769))
+            shapes.append((s, l) if rng.integers(2) else (l, s))
+        coeffs = oracle.QUINTIC
+    else:
+        shapes = [(300, 700), (700, 300), (1000, 1500), (1500, 1000), (256, 768), (33, 700)]
+        coeffs = oracle.CUBIC
+    xs = [torch.from_numpy(rng.standard_normal(sh).astype(np.float32)).to(torch.bfloat16).cuda()
+          for sh in shapes]
+    wide = nsa.ns_batched(xs, steps=5, coeffs=coeffs)
+    square = nsa.ns_batched(xs, steps=5, coeffs=coeffs, cu_budget=1 << 20)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(wide, square)):
+        assert torch.equal(a, b), (i, shapes[i])
+    # the larger ones against the oracle too (the small ones' bf16 error is
+    # discussed at test_many_small_matrices)
+    for i, sh in enumerate(shapes):
+        if min(sh) >= 256:
+            want = oracle.newton_schulz(host_f64(xs[i]), 5, coeffs)
+            assert rel_fro(host_f64(wide[i]), want) <= TOL["bf16"], (i, sh)
+
+
 @pytest.mark.parametrize("budget", [8, 24, 100])
 def test_cu_budget_gives_identical_results(budget):
     """A CU budget (fewer workgroups, each looping over tiles) changes only where
