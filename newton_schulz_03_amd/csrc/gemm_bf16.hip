@@ -550,6 +550,8 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
     const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
     const uint32_t fill = ring + ((kt + NST - 1) & (NST - 1)) * STAGEB;
     const i32x4_t rp = sp.rsrc(ks);
+    term_op(f0, 0, R);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if ((i & 3) == 0) sp.issue_one(rp, fill, i >> 2);
@@ -557,8 +559,6 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
       mfma_op(f0, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    term_op(f0, 0, R);
-    __builtin_amdgcn_sched_barrier(0);
     // slice kt+1 has landed once only slice kt+2 and the P half of kt+NST-1 remain
     wait_vm<(NST - 3) * 2 * LPO + LPO>();
     wait_lgkm0();  // this wave's reads of `stage` are done before the next refill
@@ -566,6 +566,8 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
     __builtin_amdgcn_sched_barrier(0);
     const i32x4_t rq = sq.rsrc(ks);
     const char* next = smem + ((kt + 1) & (NST - 1)) * STAGEB;
+    term_op(f1, 1, R);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if ((i & 3) == 0) sq.issue_one(rq, fill + OPB, i >> 2);
@@ -573,8 +575,6 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
       mfma_op(f1, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    term_op(f1, 1, R);
-    __builtin_amdgcn_sched_barrier(0);
   };
   using NoTerm = std::integral_constant<int, -1>;
   if constexpr (MODE == GM_GRAM) {
@@ -842,6 +842,8 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
     const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
     const uint32_t fill = ring + ((kt + NST - 1) & (NST - 1)) * STAGEW;
     const i32x4_t rp = sp.rsrc(ks);
+    term_op(f0, 0, R);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 24; ++i) {
       if ((i & 3) == 0) sp.issue_one(rp, fill, i >> 2);
@@ -849,8 +851,6 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
       mfma_op(f0, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    term_op(f0, 0, R);
-    __builtin_amdgcn_sched_barrier(0);
     // slice kt+1 has landed once only slice kt+2 and the X half of kt+NST-1 remain
     wait_vm<(NST - 3) * (LPW + LPO) + LPW>();
     wait_lgkm0();
@@ -858,6 +858,8 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
     __builtin_amdgcn_sched_barrier(0);
     const i32x4_t rq = sq.rsrc(ks);
     const char* next = smem + ((kt + 1) & (NST - 1)) * STAGEW;
+    term_op(f1, 1, R);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 24; ++i) {
       if (i % 6 == 0) sq.issue_one(rq, fill + OPBW, i / 6);
@@ -865,8 +867,6 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
       mfma_op(f1, i);
       __builtin_amdgcn_sched_barrier(0);
     }
-    term_op(f1, 1, R);
-    __builtin_amdgcn_sched_barrier(0);
   };
   using NoTerm = std::integral_constant<int, -1>;
   const int rel0 = __builtin_amdgcn_readfirstlane(8 * tr.ti + 4 * wn);
