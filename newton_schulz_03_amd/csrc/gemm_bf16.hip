@@ -388,7 +388,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
 // One output tile (tile number t of the launch).  FINAL (products only): the last product
 // of a call, storing with store_final.  FIRST (products only): the first product of a
 // call, whose iterate is still U, scaled by the norm factor as it is stored.
-template <int MODE, bool FINAL, bool FIRST>
+template <int MODE, bool FINAL, bool FIRST, bool LOOP>
 __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g, int32_t t,
                                           char* smem, int* slot) {
   const TileRef tr = decode_tile<MODE>(c, t, slot);
@@ -396,7 +396,12 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   const int64_t s_pad = d.s_pad, l_pad = d.l_pad;
   const uint16_t* Xc = static_cast<const uint16_t*>(iterate(d, g.cur));
 
-  const int lane = threadIdx.x & 63;
+  // LOOP: the lane index passes through an empty asm, so that the per-lane
+  // offsets and identity fragments derived from it are formed anew for every
+  // tile instead of being hoisted out of the tile loop and held live through
+  // the epilogue (which made the looping kernels spill more).
+  int lane = threadIdx.x & 63;
+  if constexpr (LOOP) asm volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
@@ -895,13 +900,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   __shared__ int slot;
   if constexpr (LOOP) {
     for (int32_t v = blockIdx.x; v < g.ntiles; v += gridDim.x) {
-      gemm_tile<MODE, FINAL, FIRST>(c, g, xcd_remap(v, g.ntiles), smem, &slot);
+      gemm_tile<MODE, FINAL, FIRST, true>(c, g, xcd_remap(v, g.ntiles), smem, &slot);
       __syncthreads();  // every wave is done with LDS before the next tile's loads land there
     }
   } else {
     const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
     if (t < 0) return;  // the whole block: t depends on blockIdx.x only
-    gemm_tile<MODE, FINAL, FIRST>(c, g, t, smem, &slot);
+    gemm_tile<MODE, FINAL, FIRST, false>(c, g, t, smem, &slot);
   }
 }
 
