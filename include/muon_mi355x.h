@@ -90,7 +90,11 @@ typedef struct {
    * work on other streams keeps the remaining CUs; this is for orthogonalizing
    * the dense matrices while expert compute goes on ("How PyTorch Scaled a
    * Near-1T MoE on Europe's Public Supercomputer", §Three optimizations that
-   * changed the economics, FlexShard bullet).  Results do not depend on it. */
+   * changed the economics, FlexShard bullet).  Results do not depend on it,
+   * bit for bit: with N = 0 the products that store the iterate take tiles of
+   * 256 x 384 where every matrix allows it (bf16, every long side padded to a
+   * multiple of 384), with N > 0 tiles of 256 x 256, and both add up every
+   * element the same way. */
   int32_t cu_budget;
 } muon_ns_params;
 
