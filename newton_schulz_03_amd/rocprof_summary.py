@@ -8,6 +8,11 @@ Usage:
     python -m newton_schulz_03_amd.rocprof_summary mfma DIR --workload NAME --command "..."
         DIR holds the CSV output of `rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16`:
         the matrix cores' busy fraction and issued bf16 flops per kernel.
+    python -m newton_schulz_03_amd.rocprof_summary clock DIR --workload NAME --command "..."
+        DIR holds the CSV output of `rocprofv3 --pmc GRBM_GUI_ACTIVE GRBM_COUNT
+        SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY`: per kernel,
+        the clock held during the dispatch, the matrix cores' busy share of its
+        cycles, and the share of wave time spent waiting.
     python -m newton_schulz_03_amd.rocprof_summary traffic FETCH_DIR WRITE_DIR
             --copy-bytes N --workload NAME --command "..."
         FETCH_DIR and WRITE_DIR hold the CSV output of two runs, one with
@@ -194,6 +199,47 @@ def cmd_traffic(a):
         print("```")
 
 
+# XCDs whose GRBM counts rocprofv3 sums per dispatch, and SIMDs of the chip.
+N_XCD = 8
+N_SIMD = 256 * 4
+
+
+def cmd_clock(a):
+    sums = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(dict)
+    for r in csv.DictReader(open(_one_csv(a.dir, "counter_collection.csv"))):
+        k = short_name(r["Kernel_Name"])
+        d = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        sums[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k][d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    print(f"# Clock and matrix-core busy share: {a.workload}\n")
+    print(f"Command (from the repository root):\n\n```\n{a.command}\n```\n")
+    print(f"Clock: GRBM_GUI_ACTIVE (GPU cycles, summed over the {N_XCD} XCDs) over the dispatch's "
+          f"duration.  Busy: SQ_VALU_MFMA_BUSY_CYCLES over those cycles x {N_SIMD} SIMDs.  "
+          "Waiting: SQ_WAIT_ANY over SQ_WAVE_CYCLES (waves stopped at s_waitcnt or a barrier); "
+          "issue-blocked: SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES.  Under counter collection the "
+          "dispatches run one at a time.\n")
+    print("| kernel | dispatches | avg ms | clock GHz | matrix cores busy | waves waiting | issue-blocked |")
+    print("|---|---|---|---|---|---|---|")
+    rows = []
+    for k, c in sums.items():
+        if k not in MUON_KERNELS or "GRBM_GUI_ACTIVE" not in c:
+            continue
+        n = len(disp[k])
+        dur = sum(disp[k].values()) / n
+        if dur < 1e-4:  # too short for its timestamps to give a clock
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / n / N_XCD
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n / (cyc * N_SIMD)
+        wc = c.get("SQ_WAVE_CYCLES", 0.0)
+        wait = c.get("SQ_WAIT_ANY", 0.0) / wc if wc else 0.0
+        blk = c.get("SQ_WAIT_INST_ANY", 0.0) / wc if wc else 0.0
+        rows.append((dur * n, f"| {k} | {n} | {dur * 1e3:.3f} | {cyc / dur / 1e9:.2f} | "
+                              f"{100 * busy:.1f}% | {100 * wait:.1f}% | {100 * blk:.1f}% |"))
+    for _, line in sorted(rows, reverse=True):
+        print(line)
+
+
 def read_traffic(path: str, workload: str):
     """traffic_bytes_per_launch from a summary written by `traffic`, or None when the
     summary is missing, names another workload, or predates the current kernel sources."""
@@ -233,8 +279,12 @@ def main(argv=None):
     m.add_argument("dir")
     m.add_argument("--workload", required=True)
     m.add_argument("--command", required=True)
+    k = sub.add_parser("clock")
+    k.add_argument("dir")
+    k.add_argument("--workload", required=True)
+    k.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    {"trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma, "clock": cmd_clock}[a.cmd](a)
     return 0
 
 
