@@ -84,8 +84,9 @@ struct UVec {
 
 // ---------------------------------------------------------------------------
 // k_prepare: one block per tile of the padded wide iterate: kPrepWideRows x
-// 256 for a wide matrix; 64 x 128 (short side x long side) for a tall one,
-// which is read as the user's 128 x 64 tile and transposed through LDS.  Each
+// 256 for a wide matrix; kPrepTallS x kPrepTallL (short side x long side,
+// 128 x 128) for a tall one, which is read as the user's kPrepTallL x
+// kPrepTallS tile (rows of 256 bytes) and transposed through LDS.  Each
 // thread moves 16-byte vectors v = it * 256 + threadIdx.x of the tile in
 // row-major order, so every load and store instruction of a wave covers whole
 // rows of the tile: contiguous runs of memory.  The transpose holds U already
@@ -124,8 +125,8 @@ __device__ __forceinline__ float prepare_vectors(const MatDesc& d, const ElemPar
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p) {
   constexpr int V = Elt<T>::kVec;
-  constexpr int kTallRows = 2 * kEwTile, kTallCols = kEwTile;  // the user's tile of a tall matrix
-  constexpr int kVecsTall = kTallRows * kTallCols / V / kThreads;   // 4 (bf16) or 8 (fp32)
+  constexpr int kTallRows = kPrepTallL, kTallCols = kPrepTallS;  // the user's tile of a tall matrix
+  constexpr int kVecsTall = kTallRows * kTallCols / V / kThreads;   // 8 (bf16) or 16 (fp32)
   constexpr int kVecsWide = kPrepWideRows * kWideTileCols / V / kThreads;
   constexpr int kPitch = kTallCols + 4 / static_cast<int>(sizeof(T));  // one 4-byte word of padding
   __shared__ __attribute__((aligned(16))) T tile[kTallRows][kPitch];

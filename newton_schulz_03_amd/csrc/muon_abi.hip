@@ -129,7 +129,7 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
     d.scale = static_cast<float>(std::sqrt(std::max(1.0, static_cast<double>(r) / static_cast<double>(c))));
     const int64_t ts = d.s_pad / kTile, tl = d.l_pad / kTile;
     const int64_t cnt[NPHASE] = {
-        d.tall ? static_cast<int64_t>(d.s_pad / kEwTile) * (d.l_pad / (2 * kEwTile))
+        d.tall ? static_cast<int64_t>(d.s_pad / kPrepTallS) * (d.l_pad / kPrepTallL)
                : static_cast<int64_t>(d.s_pad / kPrepWideRows) * (d.l_pad / kWideTileCols),  // PH_PREPARE
         ts * (ts + 1) / 2,                                                   // PH_SYM
         ts * tl,                                                             // PH_PROD

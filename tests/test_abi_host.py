@@ -56,10 +56,12 @@ def expected_workspace(shapes, esize):
 
     batch = len(shapes)
     desc = 112  # sizeof(MatDesc)
-    total = up(desc * batch, 256) + up(4 * 4 * (batch + 1), 256)  # 4 phase prefix arrays
+    total = up(desc * batch, 256) + up(4 * 5 * (batch + 1), 256)  # 5 phase prefix arrays
     total += up(4 * batch, 256)  # per-matrix 1 / (||U|| + eps)
-    # one partial sum of squares per 64 x 128 tile of the padded wide iterate
-    blocks = sum((up(min(r, c), 256) // 64) * (up(max(r, c), 256) // 128) for r, c in shapes)
+    # one partial sum of squares per momentum-pass tile of the padded wide
+    # iterate: 32 x 256 for a wide matrix (rows <= cols), 128 x 128 for a tall one
+    blocks = sum((up(r, 256) // 32) * (up(c, 256) // 256) if r <= c else
+                 (up(c, 256) // 128) * (up(r, 256) // 128) for r, c in shapes)
     total += up(4 * blocks, 256)
     for r, c in shapes:
         s, l = min(r, c), max(r, c)
@@ -71,7 +73,7 @@ def expected_workspace(shapes, esize):
 @pytest.mark.parametrize("dtype,esize", [(nsa.MUON_BF16, 2), (nsa.MUON_FP32, 4)])
 def test_workspace_bytes(dtype, esize):
     for shapes in [[(256, 512)], [(2048, 6144)] * 3, [(257, 771), (771, 257), (1, 5)],
-                   [(6144, 6144), (6144, 1024)]]:
+                   [(6144, 6144), (6144, 1024)], [(300, 200)] * 60 + [(2048, 6144)] * 3]:
         assert nsa.workspace_bytes(shapes, dtype) == expected_workspace(shapes, esize)
     assert nsa.workspace_bytes([], dtype) == 0
 
