@@ -549,6 +549,10 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   // Slice kt: stage kt is read; stage kt+NST-1 (the one slice kt-1 used) is
   // refilled with slice kt+NST-1, its P loads in the first half and its Q loads
   // in the second, so that the address path sees one load every few MFMAs.
+  // A term slice issues its term MFMAs first in each half, while only that
+  // half's fragments are live (after the half's products, both fragment sets
+  // would be, and the wide kernel, which adds its terms in the same order,
+  // would spill).
   auto slice = [&](int kt, auto R) {
     const int st = kt & (NST - 1);
     const char* stage = smem + st * STAGEB;
@@ -841,7 +845,10 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
 
   // One K slice: 24 steps of {memory op(s), one MFMA} per half; the X-slice
   // loads of stage kt+NST-1 go out in the first half (one every 4 MFMAs), the
-  // B-slice loads in the second (one every 6).
+  // B-slice loads in the second (one every 6).  Term MFMAs come first in their
+  // half, as in gemm_tile: issued after the products they spilled 8 dwords,
+  // and every spill reload then waited for vmcnt(0), since the compiler cannot
+  // count the loads in the inline assembly, draining the operand prefetch.
   auto slice = [&](int kt, auto R) {
     const char* stage = smem + (kt & (NST - 1)) * STAGEW;
     const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
