@@ -436,14 +436,16 @@ def test_rank_deficient_inputs(dtype):
         assert np.all(oh[zr, :] == 0) and np.all(oh[:, zc] == 0)
 
 
-@pytest.mark.parametrize("case", ["many", "cubic"])
+@pytest.mark.parametrize("case", ["many", "cubic", "long"])
 def test_wide_product_tiles_match_square_tiles(case):
     """The first and middle products run in 256 x 384 tiles when every padded
     long side is a multiple of 384; a CU budget (here larger than any grid)
     selects the 256 x 256 kernel instead.  Both accumulate every element with
     the same MFMAs in the same order, so the outputs agree bit for bit.
     many: 2100 matrices, past the batch size at which blocks find their matrix
-    by binary search; cubic: (1.5, -0.5, 0), where the product reads A itself."""
+    by binary search; cubic: (1.5, -0.5, 0), where the product reads A itself;
+    long: a long side of 65280 = 170 x 384, near the largest allowed, in both
+    orientations."""
     rng = np.random.default_rng(99)
     if case == "many":
         shapes = []
@@ -451,9 +453,12 @@ def test_wide_product_tiles_match_square_tiles(case):
             s, l = int(rng.integers(1, 41)), int(rng.integers(513, 769))
             shapes.append((s, l) if rng.integers(2) else (l, s))
         coeffs = oracle.QUINTIC
-    else:
+    elif case == "cubic":
         shapes = [(300, 700), (700, 300), (1000, 1500), (1500, 1000), (256, 768), (33, 700)]
         coeffs = oracle.CUBIC
+    else:
+        shapes = [(256, 65280), (65280, 256)]
+        coeffs = oracle.QUINTIC
     xs = [torch.from_numpy(rng.standard_normal(sh).astype(np.float32)).to(torch.bfloat16).cuda()
           for sh in shapes]
     wide = nsa.ns_batched(xs, steps=5, coeffs=coeffs)
