@@ -80,6 +80,14 @@ __device__ __forceinline__ u32x4_t ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, const u32x4_t& v) {
   *(GLOBAL_AS u32x4_t*)(p) = v;
 }
+// The same with the nontemporal hint, for data that one call reads or writes
+// once (the momentum pass's G, M and M').
+__device__ __forceinline__ u32x4_t ld16_nt(const void* p) {
+  return __builtin_nontemporal_load((const GLOBAL_AS u32x4_t*)(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, const u32x4_t& v) {
+  __builtin_nontemporal_store(v, (GLOBAL_AS u32x4_t*)(p));
+}
 
 // Sum over a wavefront of 64 lanes with a fixed butterfly order (deterministic).
 __device__ __forceinline__ float wave_sum(float v) {

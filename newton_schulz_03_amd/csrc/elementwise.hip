@@ -31,8 +31,9 @@ struct UVec {
     full = r < d.rows && d.vec_ok && c0 + V <= d.cols;
     if (!full) return;
     const int64_t off = r * d.cols + c0;
-    a = ld16(static_cast<const T*>(d.src) + off);
-    if (p.mode == MODE_STEP) m = ld16(static_cast<const T*>(d.mom) + off);
+    // read once: nontemporal (measured: the pass 3% faster on 96 x 2048x6144)
+    a = ld16_nt(static_cast<const T*>(d.src) + off);
+    if (p.mode == MODE_STEP) m = ld16_nt(static_cast<const T*>(d.mom) + off);
   }
 
   // u <- U over the vector (zeros outside the matrix); stores M' (step).  U is
@@ -50,7 +51,7 @@ struct UVec {
 #pragma unroll
       for (int e = 0; e < V; ++e) mn[e] = p.beta * mo[e] + g[e];
       const u32x4_t packed = f32_to_vec<T>(mn);
-      st16(static_cast<T*>(d.mom) + r * d.cols + c0, packed);
+      st16_nt(static_cast<T*>(d.mom) + r * d.cols + c0, packed);  // not read again this call
       vec_to_f32<T>(packed, u);
       if (p.nesterov) {
 #pragma unroll
