@@ -474,6 +474,32 @@ def test_wide_product_tiles_match_square_tiles(case):
             assert rel_fro(host_f64(wide[i]), want) <= TOL["bf16"], (i, sh)
 
 
+@pytest.mark.parametrize("steps", [2, 3])
+def test_wide_first_product_feeds_square_last_product(steps):
+    """With 2 steps the wide first product hands its iterate straight to the
+    256 x 256 fused last product; with 3 one wide middle product sits between.
+    Orthogonalization and full step, bit for bit against the 256 x 256 path."""
+    shapes = [(300, 700), (700, 300), (1024, 1536), (513, 257)]
+    wl = _wl("muon", "bf16", shapes)
+    ins = device_inputs(wl)
+    g = [d["g"] for d in ins]
+    wide = nsa.ns_batched(g, steps=steps)
+    square = nsa.ns_batched(g, steps=steps, cu_budget=1 << 20)
+    w0 = [d["w"].clone() for d in ins]
+    m0 = [d["m"].clone() for d in ins]
+    w1 = [d["w"].clone() for d in ins]
+    m1 = [d["m"].clone() for d in ins]
+    nsa.step_batched(w0, g, m0, steps=steps, nesterov=True)
+    nsa.step_batched(w1, g, m1, steps=steps, nesterov=True, cu_budget=1 << 20)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(wide[i], square[i]), i
+        assert torch.equal(w0[i], w1[i]) and torch.equal(m0[i], m1[i]), i
+    for i, sh in enumerate(shapes):
+        want = oracle.newton_schulz(host_f64(g[i]), steps)
+        assert rel_fro(host_f64(wide[i]), want) <= TOL["bf16"], (i, sh)
+
+
 @pytest.mark.parametrize("budget", [8, 24, 100])
 def test_cu_budget_gives_identical_results(budget):
     """A CU budget (fewer workgroups, each looping over tiles) changes only where
