@@ -5,7 +5,6 @@ The HIP library and its Python binding never import it.
 """
 from .muon_oracle import (  # noqa: F401
     CUBIC, DEFAULT_EPS, QUINTIC, apply_update, frobenius_norm, is_tall, momentum,
-    muon_step, muon_step_batched, nesterov_direction, newton_schulz, normalize,
-    ns_batched, update_scale,
+    muon_step, nesterov_direction, newton_schulz, normalize, update_scale,
 )
-from .adamw_oracle import adamw_batched, adamw_step  # noqa: F401,E402
+from .adamw_oracle import adamw_step  # noqa: F401,E402

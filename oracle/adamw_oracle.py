@@ -21,7 +21,7 @@ Each step is written out in that order, in float64 numpy, elementwise.
 """
 from __future__ import annotations
 
-from typing import Sequence, Tuple
+from typing import Tuple
 
 import numpy as np
 
@@ -43,8 +43,3 @@ def adamw_step(p, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
     p = p - lr * m_hat / (np.sqrt(v_hat) + eps)
     return p, m, v
 
-
-def adamw_batched(ps: Sequence, gs: Sequence, ms: Sequence, vs: Sequence, **kw):
-    """adamw_step over a batch; returns lists (p', m', v')."""
-    out = [adamw_step(p, g, m, v, **kw) for p, g, m, v in zip(ps, gs, ms, vs)]
-    return [o[0] for o in out], [o[1] for o in out], [o[2] for o in out]

@@ -108,12 +108,3 @@ def muon_step(w, g, m, lr: float = 0.02, beta: float = 0.95, nesterov: bool = Fa
     o = newton_schulz(u, steps, coeffs, eps)
     return apply_update(w, o, lr), m_new, o
 
-
-def ns_batched(xs, steps: int, coeffs: Sequence[float] = QUINTIC, eps: float = DEFAULT_EPS):
-    """The orthogonalization alone over a ragged batch, one matrix at a time."""
-    return [newton_schulz(x, steps, coeffs, eps) for x in xs]
-
-
-def muon_step_batched(ws, gs, ms, **kw):
-    """The full step over a ragged batch, one matrix at a time."""
-    return [muon_step(w, g, m, **kw) for w, g, m in zip(ws, gs, ms)]
