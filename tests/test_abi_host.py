@@ -187,3 +187,18 @@ def test_adamw_validation(lib):
     assert adamw_call(lib, ws=0) == E.MUON_ERR_WORKSPACE
     assert adamw_call(lib, ws_bytes=8) == E.MUON_ERR_WORKSPACE
     assert adamw_call(lib, ws=FAKE + (1 << 20) + 16) == E.MUON_ERR_INVALID_ARG
+
+
+def test_hbm_stream_validation(lib):
+    """The measurement stream rejects bad counts, sizes and pointers before any
+    launch; zero bytes is a no-op."""
+    ins = _ptr_array([FAKE, FAKE + 16384])
+    outs = _ptr_array([FAKE + 2 * 16384, FAKE + 3 * 16384])
+    for n_in, n_out, nbytes, args in [(0, 1, 16384, (ins, outs)), (3, 1, 16384, (ins, outs)),
+                                      (1, 0, 16384, (ins, outs)), (1, 3, 16384, (ins, outs)),
+                                      (1, 1, 16000, (ins, outs)), (1, 1, 16384, (None, outs)),
+                                      (1, 1, 16384, (_ptr_array([FAKE + 8]), outs)),
+                                      (2, 2, 16384, (ins, _ptr_array([FAKE, 0])))]:
+        st = lib.muon_hbm_stream(n_in, args[0], n_out, args[1], nbytes, 0, None)
+        assert st == nsa.MUON_ERR_INVALID_ARG, (n_in, n_out, nbytes)
+    assert lib.muon_hbm_stream(2, ins, 2, outs, 0, 1, None) == nsa.MUON_OK

@@ -13,7 +13,9 @@ import torch
 import newton_schulz_03_amd as nsa
 import oracle
 import workloads
-from parity_util import TOL, device_inputs, host_f64, rel_fro, singular_values
+from parity_util import (TOL, check_blocks, device_inputs, host_f64, momentum_within_rounding,
+                         rel_fro, singular_values, update_step)
+from rounding_bounds import ns_with_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -28,18 +30,19 @@ def _wl(kind, dtype, shapes, **kw):
     return dataclasses.replace(base, **kw)
 
 
-def _ns_check(dtype, shapes, steps=5, coeffs=oracle.QUINTIC, tol=None, eps=1e-7):
+def _ns_check(dtype, shapes, steps=5, coeffs=oracle.QUINTIC, tol=None, eps=1e-7, cu_budget=0):
+    """Orthogonalize a Gaussian batch and hold every 256 x 256 block of every
+    output to the tolerance against the oracle."""
     wl = _wl("gauss", dtype, shapes, steps=steps, coeffs=coeffs)
     ins = device_inputs(wl)
     xs = [d["x"] for d in ins]
-    outs = nsa.ns_batched(xs, steps=steps, coeffs=coeffs, eps=eps)
+    outs = nsa.ns_batched(xs, steps=steps, coeffs=coeffs, eps=eps, cu_budget=cu_budget)
     torch.cuda.synchronize()
-    errs = []
-    for x, o in zip(xs, outs):
-        want = oracle.newton_schulz(host_f64(x), steps, coeffs, eps)
-        errs.append(rel_fro(host_f64(o), want))
     tol = TOL[dtype] if tol is None else tol
-    assert max(errs) <= tol, list(zip(shapes, errs))
+    errs = []
+    for x, o, sh in zip(xs, outs, shapes):
+        want = oracle.newton_schulz(host_f64(x), steps, coeffs, eps)
+        errs.append(check_blocks(host_f64(o), want, tol, what=f"{dtype} {sh}"))
     return errs
 
 
@@ -178,6 +181,67 @@ def test_launch_sequence(dtype, steps, call):
     assert got == want
 
 
+# Batches for the elementwise bound test.  WIDE_TILES: every padded long side is
+# a multiple of 384, so the first and middle products of a bf16 call run in
+# 256 x 384 tiles; SQUARE_TILES: not, so every product runs in 256 x 256 tiles.
+# Both span several tiles with ragged tails, in both orientations.
+WIDE_TILES = [(300, 700), (700, 300), (1000, 1500), (1500, 1000), (40, 1300), (600, 740)]
+SQUARE_TILES = [(520, 1040), (1040, 520), (257, 771), (33, 65), (600, 600), (1, 300)]
+# Iterations whose terms do not cancel, so that the first-order rounding bound
+# is tight enough to gate every element: one to three steps with a positive
+# polynomial (Gram, A^2 with its (b/c) A term, the a X term), the a X term
+# alone over two steps, and one step of the Gram and product alone.
+BOUND_CASES = [((0.5, 0.25, 0.125), 1), ((0.5, 0.25, 0.125), 2), ((0.5, 0.25, 0.125), 3),
+               ((1.0, 0.0, 0.0), 2), ((0.0, 1.0, 0.0), 1)]
+
+
+def _check_bound(got, u, steps, coeffs, what, extra_rel=0.0):
+    """Every element of got (float64) within the rounding bound of the exact
+    iteration on the bf16 input u, which must be the oracle's result."""
+    want = oracle.newton_schulz(u, steps, coeffs)
+    x, e = ns_with_bound(u, steps, coeffs)
+    assert np.max(np.abs(x - want)) <= 1e-12 * max(1.0, np.max(np.abs(want))), what
+    bound = e + extra_rel * (np.abs(want) + e)
+    ratio = np.abs(got - want) / np.where(bound > 0, bound, np.inf)
+    bad = np.abs(got - want) > bound
+    assert not bad.any(), (what, int(bad.sum()), float(np.max(ratio)),
+                           tuple(int(i) for i in np.argwhere(bad)[0]))
+    return float(np.max(ratio))
+
+
+@pytest.mark.parametrize("budget", [0, 24])
+@pytest.mark.parametrize("batch", ["wide_tiles", "square_tiles"])
+@pytest.mark.parametrize("coeffs,steps", BOUND_CASES)
+def test_bf16_every_element_within_rounding_bound(coeffs, steps, batch, budget):
+    """bf16 products checked element by element: the output of the
+    orthogonalize-only call, and the step's own O (read back from a step with
+    W = 0, M = 0, where W' = rnd(-lr*scale*O)), each within the first-order
+    rounding bound around the oracle's result.  Covers the first, middle and
+    fused last products in both tile widths, the Gram's mirror stores and
+    diagonal tiles, A^2 with its (b/c) A term, both orientations, and with a CU
+    budget the looping kernels."""
+    shapes = WIDE_TILES if batch == "wide_tiles" else SQUARE_TILES
+    wl = _wl("gauss", "bf16", shapes, steps=steps, coeffs=coeffs)
+    xs = [d["x"] for d in device_inputs(wl)]
+    outs = nsa.ns_batched(xs, steps=steps, coeffs=coeffs, cu_budget=budget)
+    wz = [torch.zeros_like(x) for x in xs]
+    mz = [torch.zeros_like(x) for x in xs]
+    lr = 0.5
+    nsa.step_batched(wz, xs, mz, lr=lr, beta=0.95, steps=steps, coeffs=coeffs, cu_budget=budget)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for x, o, w1, m1, sh in zip(xs, outs, wz, mz, shapes):
+        u = host_f64(x)
+        assert torch.equal(m1, x), sh  # M' = 0.95 * 0 + G exactly
+        worst = max(worst, _check_bound(host_f64(o), u, steps, coeffs, ("ns", sh)))
+        # W' = rnd(0 - step * O_stored) with step = lr * scale formed in fp32: one more
+        # bf16 rounding and a few fp32 ones on top of O's own bound
+        o_step = -host_f64(w1) / update_step(*sh, lr)
+        worst = max(worst, _check_bound(o_step, u, steps, coeffs, ("step", sh),
+                                        extra_rel=2.0 ** -8 + 4 * 2.0 ** -24))
+    print(f"  worst |error| / bound = {worst:.3f}")
+
+
 @pytest.mark.parametrize("coeffs,steps", [((1.0, 0.0, 0.0), 1), ((0.0, 1.0, 0.0), 1),
                                           ((0.0, 0.0, 1.0), 1), ((0.5, 0.25, -0.125), 2),
                                           (oracle.QUINTIC, 0)])
@@ -217,7 +281,7 @@ def test_step_parity(dtype, nesterov, steps):
         w_ref, m_ref, o_ref = oracle.muon_step(w0[i], g0[i], m0[i], lr=wl.lr, beta=wl.beta,
                                                nesterov=nesterov, steps=steps)
         assert rel_fro(host_f64(m[i]), m_ref) <= TOL[dtype] / 4
-        assert rel_fro(host_f64(o_gpu[i]), o_ref) <= TOL[dtype]
+        check_blocks(host_f64(o_gpu[i]), o_ref, TOL[dtype], what=f"{dtype} step O {(r, c)}")
         # W' is the stored rounding of W - lr*scale*O evaluated in fp32: within one ulp of
         # the result, plus fp32 evaluation error relative to the operands (lr and the
         # product are rounded to fp32, which matters where W and lr*scale*O cancel)
@@ -328,7 +392,11 @@ def test_workspace_reuse_across_shapes():
 
 @pytest.mark.parametrize("dtype,nesterov", [("bf16", False), ("bf16", True), ("fp32", False)])
 def test_step_momentum_in_host_memory(dtype, nesterov):
-    """The momentum kept in pinned host memory gives bit-identical results."""
+    """The momentum kept in pinned host memory gives bit-identical results to
+    the momentum in HBM, and both are held to the oracle: M' element by element
+    (within its storage rounding), and the step's own O (from a second step
+    with W = 0 and the momentum in host memory, which stores rnd(-lr*scale*O))
+    per 256 x 256 block."""
     shapes = [(300, 700), (700, 300), (513, 257), (64, 2048)]
     wl = _wl("muon", dtype, shapes, nesterov=nesterov)
     ins = device_inputs(wl)
@@ -337,13 +405,27 @@ def test_step_momentum_in_host_memory(dtype, nesterov):
     g = [d["g"] for d in ins]
     w_host = [d["w"].clone() for d in ins]
     m_host = [d["m"].cpu().pin_memory() for d in ins]
+    wz = [torch.zeros_like(d["w"]) for d in ins]
+    mz_host = [d["m"].cpu().pin_memory() for d in ins]
     nsa.step_batched(w_dev, g, m_dev, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5)
     nsa.step_batched(w_host, g, m_host, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5,
+                     momentum_host=True)
+    nsa.step_batched(wz, g, mz_host, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5,
                      momentum_host=True)
     torch.cuda.synchronize()
     for i in range(len(shapes)):
         assert torch.equal(w_dev[i], w_host[i]), i
         assert torch.equal(m_dev[i].cpu(), m_host[i]), i
+        assert torch.equal(mz_host[i], m_host[i]), i
+    for i, sh in enumerate(shapes):
+        gh, mh = host_f64(g[i]), host_f64(ins[i]["m"])
+        assert not momentum_within_rounding(mh, gh, host_f64(m_host[i]), wl.beta, dtype).any(), sh
+        _, _, o_ref = oracle.muon_step(np.zeros_like(gh), gh, mh, lr=wl.lr, beta=wl.beta,
+                                       nesterov=nesterov, steps=5)
+        o_step = -host_f64(wz[i]) / update_step(*sh, wl.lr)
+        # the step rounds M' (and U = G + beta*M' with Nesterov) to the dtype, the
+        # oracle keeps them in float64: a difference far below the tolerance
+        check_blocks(o_step, o_ref, TOL[dtype], what=f"{dtype} host momentum, step O, {sh}")
     # a second step from the state left in host memory
     nsa.step_batched(w_dev, g, m_dev, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5)
     nsa.step_batched(w_host, g, m_host, lr=wl.lr, beta=wl.beta, nesterov=nesterov, steps=5,
@@ -503,7 +585,10 @@ def test_wide_first_product_feeds_square_last_product(steps):
 @pytest.mark.parametrize("budget", [8, 24, 100])
 def test_cu_budget_gives_identical_results(budget):
     """A CU budget (fewer workgroups, each looping over tiles) changes only where
-    tiles run: the bits are the same, for the orthogonalization and the step."""
+    tiles run: the bits are the same, for the orthogonalization and the step.
+    The looping kernels' results are also held to the oracle directly: every
+    256 x 256 block of the orthogonalization, of the step's own O (a step with
+    W = 0 stores rnd(-lr*scale*O)) and the momentum element by element."""
     shapes = [(300, 700), (700, 300), (1024, 1536), (513, 257)]
     wl = _wl("muon", "bf16", shapes)
     ins = device_inputs(wl)
@@ -516,7 +601,19 @@ def test_cu_budget_gives_identical_results(budget):
     m1 = [d["m"].clone() for d in ins]
     nsa.step_batched(w0, g, m0, steps=5)
     nsa.step_batched(w1, g, m1, steps=5, cu_budget=budget)
+    wz = [torch.zeros_like(t) for t in w1]
+    mz = [d["m"].clone() for d in ins]
+    nsa.step_batched(wz, g, mz, steps=5, cu_budget=budget, lr=wl.lr)
     torch.cuda.synchronize()
     for i in range(len(shapes)):
         assert torch.equal(full[i], some[i]), i
         assert torch.equal(w0[i], w1[i]) and torch.equal(m0[i], m1[i]), i
+        assert torch.equal(mz[i], m1[i]), i
+    for i, sh in enumerate(shapes):
+        gh, mh = host_f64(g[i]), host_f64(ins[i]["m"])
+        check_blocks(host_f64(some[i]), oracle.newton_schulz(gh, 5), TOL["bf16"],
+                     what=f"ns, budget {budget}, {sh}")
+        assert not momentum_within_rounding(mh, gh, host_f64(m1[i]), wl.beta, "bf16").any(), sh
+        _, _, o_ref = oracle.muon_step(np.zeros_like(gh), gh, mh, lr=wl.lr, beta=wl.beta, steps=5)
+        o_step = -host_f64(wz[i]) / update_step(*sh, wl.lr)
+        check_blocks(o_step, o_ref, TOL["bf16"], what=f"step O, budget {budget}, {sh}")
