@@ -7,8 +7,16 @@ normalization, 5 Newton-Schulz iterations and the weight update for every
 matrix, on synthetic seeded inputs already resident in HBM.  The default
 workload is 96 bf16 expert matrices of 2048 x 6144.  Prints one JSON line.
 
-The per-kernel durations come from HIP events that the library records around
-each launch on the same stream during the timed region.
+The headline is timed with HIP events around the K steps alone, with the
+library's per-kernel instrumentation off.  The per-kernel durations come from a
+second pass of K steps in which the library records HIP events around each
+launch, on the stream the kernels run on.
+
+    python bench.py --hbm-ceiling
+
+measures the plain HBM stream (1 and 2 reads, 1 and 2 writes, 16-byte
+lane-contiguous vectors, with and without the nontemporal hint) that the
+bandwidth-bound kernels are held against.
 """
 from __future__ import annotations
 
@@ -97,6 +105,10 @@ def cpu_baseline(wl, seconds: float, max_sample: int):
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
     except Exception:  # pragma: no cover - threadpoolctl missing
         cores = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - not Linux
+        affinity = os.cpu_count() or 1
     dt = 0.0
     sample = 0
     while sample < min(max_sample, wl.batch) and (sample == 0 or dt < seconds):
@@ -111,7 +123,8 @@ def cpu_baseline(wl, seconds: float, max_sample: int):
         dt += time.perf_counter() - t0
         sample += 1
     shapes = sorted({tuple(s) for s in wl.shapes[:sample]})
-    return {"value": round(sample / dt, 4), "unit": "matrices/s", "cores": cores, "kind": "oracle",
+    return {"value": round(sample / dt, 4), "unit": "matrices/s", "cores": cores,
+            "host_cpus": os.cpu_count(), "cpus_in_affinity": affinity, "kind": "oracle",
             "sample": f"first {sample} of {wl.batch} matrices {shapes} of {wl.name}, full step "
                       f"in float64 numpy, {dt:.1f} s of oracle time", "seconds": round(dt, 2)}
 
@@ -211,6 +224,43 @@ def bench_adamw(args, wl) -> int:
                                   "sample": f"first {j} of {wl.batch} tensors ({done} elements), "
                                             f"float64 numpy, {dt:.1f} s"}
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_hbm_ceiling(args) -> int:
+    """The plain HBM stream of the library's measurement kernel, per pattern:
+    GB/s and the fraction of 8 TB/s, median of `steps` launches over buffers
+    of the momentum pass's per-tensor size on the benchmark workload."""
+    import torch
+
+    import newton_schulz_03_amd as nsa
+
+    dev = torch.device("cuda:0")
+    n = args.hbm_bytes
+    bufs = [torch.empty(n, dtype=torch.uint8, device=dev).fill_(k + 1) for k in range(4)]
+    out = {}
+    for n_in, n_out in ((1, 1), (2, 1), (2, 2)):
+        for nt in (False, True):
+            ins, outs = bufs[:n_in], bufs[2:2 + n_out]
+            for _ in range(max(1, args.warmup)):
+                nsa.hbm_stream(ins, outs, nontemporal=nt)
+            times = []
+            for _ in range(args.steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                nsa.hbm_stream(ins, outs, nontemporal=nt)
+                b.record()
+                torch.cuda.synchronize(dev)
+                times.append(a.elapsed_time(b))
+            ms = sorted(times)[len(times) // 2]
+            gbs = (n_in + n_out) * n / (ms * 1e-3) / 1e9
+            out[f"{n_in}r{n_out}w{'_nt' if nt else ''}"] = {
+                "ms": round(ms, 4), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    for k in range(2):
+        assert torch.equal(bufs[2 + k], bufs[k])  # the last (2r2w) copy moved every byte
+    print(json.dumps({"metric": "HBM read+write stream ceiling (plain copy kernel)",
+                      "unit": "GB/s", "bytes_per_stream": n, "peak": PEAK_HBM_GBS,
+                      "median_of": args.steps, "patterns": out}), flush=True)
     return 0
 
 
@@ -368,6 +418,11 @@ def main(argv=None) -> int:
     ap.add_argument("--momentum-host", action="store_true",
                     help="keep the momentum in pinned host memory (the GPU reads and writes it "
                          "in place over the host link)")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="measure the plain HBM stream ceiling of the bandwidth-bound kernels")
+    ap.add_argument("--hbm-bytes", type=int, default=96 * 2048 * 6144 * 2,
+                    help="bytes per stream for --hbm-ceiling (default: one bf16 tensor of the "
+                         "benchmark workload, 96 x 2048 x 6144)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling hardware traffic counters)")
@@ -392,6 +447,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.overlap:
         return bench_overlap(args)
+    if args.hbm_ceiling:
+        return bench_hbm_ceiling(args)
     adamw = workloads.adamw_workloads()
     if args.workload in adamw:
         return bench_adamw(args, adamw[args.workload])
@@ -432,8 +489,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    nsa.timing_reset()
-    nsa.timing_enable(True)
+    # the headline: K steps, no per-kernel instrumentation
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     start.record()
@@ -441,11 +497,24 @@ def main(argv=None) -> int:
         step()
     end.record()
     torch.cuda.synchronize(dev)
-    nsa.timing_enable(False)
-    kern = nsa.timing_read()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    # per-kernel durations: another K steps with HIP events around every launch
+    nsa.timing_reset()
+    nsa.timing_enable(True)
+    torch.cuda.synchronize(dev)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize(dev)
+    nsa.timing_enable(False)
+    kern = nsa.timing_read()
+    instrumented_ms = t_start.elapsed_time(t_end) / args.steps
+    print(f"[bench] per-kernel pass: {instrumented_ms:.3f} ms/step with per-launch events",
+          file=sys.stderr, flush=True)
 
     esize = 2 if wl.dtype == "bf16" else 4
     fl = [ns_flops(s, wl.steps, c != 0.0) for s in shapes]
@@ -504,6 +573,7 @@ def main(argv=None) -> int:
         "ns_effective_tflops": round(alg_total / (total_ms / args.steps * 1e-3) / 1e12, 1),
         "ns_mfma_frac_whole_step": round(alg_total / (total_ms / args.steps * 1e-3) / 1e12 / peak, 4),
         "ns_kernels_ms_per_step": round(ns_ms, 3),
+        "per_kernel_pass_ms_per_step": round(instrumented_ms, 3),
         "kernels": per_kernel,
     }
     if args.copy_calibration_mb > 0:

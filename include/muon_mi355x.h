@@ -35,12 +35,16 @@
  *    point.
  *  - The caller owns every buffer, the workspace included.  The library
  *    allocates no device memory and keeps no pointer after it returns; it owns
- *    only a small ring of pinned host staging buffers for the descriptor
- *    upload, allocated on first use and kept until the process ends.
+ *    only a pool of small pinned host staging buffers for the descriptor
+ *    upload, allocated on first use and kept until the process ends.  A call
+ *    takes a staging buffer whose upload has completed, or a new one when all
+ *    are in flight (at most 256 per device).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
- *    and the call returns without synchronizing.  Buffers must stay alive and
- *    untouched until the stream has finished the work.  Two calls may run
- *    concurrently only with distinct workspaces.
+ *    and the call returns without waiting for the GPU, except with more than
+ *    256 calls in flight on one device, when it waits for the oldest one's
+ *    descriptor upload.  Buffers must stay alive and untouched until the
+ *    stream has finished the work.  Two calls may run concurrently only with
+ *    distinct workspaces.
  *  - Every argument is validated before anything is enqueued; on any error
  *    nothing is launched and the outputs are untouched.  batch == 0 is a no-op
  *    that returns MUON_OK.
@@ -225,6 +229,22 @@ typedef enum {
 int32_t muon_timing_enable(int32_t enable);
 int32_t muon_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
 int32_t muon_timing_reset(void);
+
+/*
+ * Measurement aid: a plain HBM stream with the access pattern of the momentum
+ * pass (16-byte vectors, lane-contiguous, every load of a block issued before
+ * its first store), for the read + write ceiling that the bandwidth-bound
+ * kernels are held against.  Output k receives input k % n_in, except that
+ * with two inputs and one output it receives their bitwise XOR; `bytes` bytes
+ * each, with the nontemporal hint when `nontemporal` is 1.
+ *   n_in, n_out  1 or 2
+ *   in, out      host arrays of 16-byte aligned device pointers
+ *   bytes        a multiple of 16384 (0: no-op)
+ * Returns MUON_OK, MUON_ERR_INVALID_ARG (nothing launched) or MUON_ERR_HIP
+ * (launch failure; muon_last_error_detail() is not set by this call).
+ */
+int32_t muon_hbm_stream(int32_t n_in, const void* const* in, int32_t n_out, void* const* out,
+                        size_t bytes, int32_t nontemporal, void* stream);
 
 /* Static string naming a status code. */
 const char* muon_status_string(int32_t status);

@@ -25,7 +25,7 @@ CUBIC = (1.5, -0.5, 0.0)
 EXPORTED = ("muon_workspace_bytes", "muon_ns_batched", "muon_step_batched",
             "muon_adamw_workspace_bytes", "muon_adamw_batched",
             "muon_status_string", "muon_last_error_detail", "muon_timing_enable",
-            "muon_timing_read", "muon_timing_reset")
+            "muon_timing_read", "muon_timing_reset", "muon_hbm_stream")
 KERNELS = ("prepare", "norm", "gram", "poly", "prod", "finish", "adamw", "prod_finish", "prod_first")
 
 
@@ -92,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_timing_read.restype = i32
     lib.muon_timing_reset.argtypes = []
     lib.muon_timing_reset.restype = i32
+    lib.muon_hbm_stream.argtypes = [i32, vpp, i32, vpp, sz, i32, vp]
+    lib.muon_hbm_stream.restype = i32
     _lib_handle = lib
     return lib
 
@@ -311,6 +313,26 @@ def adamw_batched(params: Sequence, grads: Sequence, exp_avgs: Sequence, exp_avg
                                     ctypes.byref(prm), ctypes.c_void_p(workspace.data_ptr()),
                                     workspace.numel(), ctypes.c_void_p(_stream_handle(dev)))
     _check(st, "muon_adamw_batched")
+
+
+def hbm_stream(ins: Sequence, outs: Sequence, nontemporal: bool = False) -> None:
+    """Plain HBM stream (measurement aid): outs[k] <- ins[k % len(ins)] (two inputs
+    into one output: their bitwise XOR), on the current stream.  1 or 2 inputs
+    and outputs, uint8 device tensors of one size, a multiple of 16384 bytes."""
+    import torch
+
+    ins, outs = list(ins), list(outs)
+    n = ins[0].numel() * ins[0].element_size()
+    for t in ins + outs:
+        if t.device.type != "cuda" or not t.is_contiguous() or t.numel() * t.element_size() != n:
+            raise ValueError("hbm_stream: contiguous device tensors of one size")
+    dev = ins[0].device
+    with torch.cuda.device(dev):
+        st = load_library().muon_hbm_stream(len(ins), _ptr_array([t.data_ptr() for t in ins]),
+                                            len(outs), _ptr_array([t.data_ptr() for t in outs]),
+                                            n, 1 if nontemporal else 0,
+                                            ctypes.c_void_p(_stream_handle(dev)))
+    _check(st, "muon_hbm_stream")
 
 
 def timing_enable(on: bool = True) -> None:

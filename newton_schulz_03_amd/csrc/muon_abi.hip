@@ -192,25 +192,58 @@ void bind(Plan& pl, char* ws) {
   }
 }
 
-// Pinned host staging for the descriptor upload: a ring of slots per device,
-// each guarded by an event recorded after its copy, so that a slot is reused
-// only once the stream has consumed it.
+// Pinned host staging for the descriptor upload: a pool of slots per device,
+// each guarded by an event recorded after its copy.  A call takes a slot whose
+// copy has completed (asked without waiting) or, when every slot still has a
+// copy in flight, a new one, so that the call does not wait for the GPU; only
+// past kMaxSlots calls in flight on one device does it wait for the oldest.
 struct Slot {
   void* host = nullptr;
   size_t cap = 0;
   hipEvent_t done = nullptr;
   bool pending = false;
 };
-constexpr int kRing = 8;
-struct Ring {
-  Slot slot[kRing];
-  int next = 0;
+constexpr size_t kMaxSlots = 256;
+struct Pool {
+  std::vector<Slot> slot;
+  size_t oldest = 0;  // round-robin start of the search, and the slot waited for when full
 };
-std::mutex g_ring_mu;
-std::map<int, Ring> g_rings;
+std::mutex g_pool_mu;
+std::map<int, Pool> g_pools;
 
 int32_t hip_fail(hipError_t e, const char* what) {
   return fail(MUON_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+// A slot of `pool` whose previous copy (if any) has completed; index in *idx.
+int32_t free_slot(Pool& pool, size_t* idx) {
+  const size_t n = pool.slot.size();
+  for (size_t k = 0; k < n; ++k) {
+    const size_t i = (pool.oldest + k) % n;
+    Slot& s = pool.slot[i];
+    if (!s.pending) {
+      *idx = i;
+      return MUON_OK;
+    }
+    const hipError_t q = hipEventQuery(s.done);
+    if (q == hipSuccess) {
+      s.pending = false;
+      *idx = i;
+      return MUON_OK;
+    }
+    if (q != hipErrorNotReady) return hip_fail(q, "hipEventQuery (staging slot)");
+  }
+  if (n < kMaxSlots) {
+    pool.slot.emplace_back();
+    *idx = n;
+    return MUON_OK;
+  }
+  Slot& s = pool.slot[pool.oldest % n];
+  const hipError_t e = hipEventSynchronize(s.done);
+  if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging slot)");
+  s.pending = false;
+  *idx = pool.oldest % n;
+  return MUON_OK;
 }
 
 // Copies `bytes` composed by `fill` into a pinned slot, then to `dst` on `stream`.
@@ -219,18 +252,16 @@ int32_t stage_upload(size_t bytes, Fill fill, void* dst, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_ring_mu);
-  Ring& ring = g_rings[dev];
-  Slot& s = ring.slot[ring.next];
-  ring.next = (ring.next + 1) % kRing;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  Pool& pool = g_pools[dev];
+  size_t idx = 0;
+  int32_t st = free_slot(pool, &idx);
+  if (st != MUON_OK) return st;
+  Slot& s = pool.slot[idx];
+  pool.oldest = (idx + 1) % pool.slot.size();
   if (s.done == nullptr) {
     e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
-  }
-  if (s.pending) {
-    e = hipEventSynchronize(s.done);
-    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (staging slot)");
-    s.pending = false;
   }
   if (s.cap < bytes) {
     if (s.host) (void)hipHostFree(s.host);
