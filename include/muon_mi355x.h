@@ -148,6 +148,28 @@ int32_t muon_ns_batched(int32_t batch, const int64_t* rows, const int64_t* cols,
                         void* stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * orthogonalization as muon_ns_batched (same kernels, bit-identical results),
+ * with no workspace argument: the workspace is a library-owned array of
+ * MUON_NOALLOC_MAX_WORKSPACE bytes in device memory (one per GPU the library
+ * runs on, held until the process ends).  The call allocates no device or
+ * pinned memory and creates no HIP objects; it enqueues only kernel launches
+ * on `stream` (the descriptor table travels as kernel arguments) and takes no
+ * part in per-kernel timing.
+ *   Arguments as muon_ns_batched.  A batch whose muon_workspace_bytes() exceeds
+ *   MUON_NOALLOC_MAX_WORKSPACE returns MUON_ERR_WORKSPACE and launches nothing.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a GPU
+ *   (on different streams, or from different threads) race and give undefined
+ *   results.  Calls in order on one stream are safe; the array keeps the last
+ *   call's contents, and every call writes each part it reads before reading it.
+ */
+#define MUON_NOALLOC_MAX_WORKSPACE ((size_t)256 << 20)
+int32_t muon_ns_batched_noalloc(int32_t batch, const int64_t* rows, const int64_t* cols,
+                                const void* const* x, void* const* out, int32_t dtype,
+                                const muon_ns_params* p, void* stream);
+
+/*
  * One Muon step over a ragged batch, in place on w[i] and m[i].
  *   w           host array[batch] of device pointers to the weights (updated in place)
  *   g           host array[batch] of device pointers to the gradients (read only)

@@ -7,6 +7,6 @@ from ._binding import (  # noqa: F401
     CUBIC, EXPORTED, HEADER_PATH, LIB_PATH, MAX_DIM, MUON_BF16, MUON_ERR_HIP,
     MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_FP32, MUON_OK, QUINTIC,
     MuonError, NsParams, StepParams, allocate_workspace, last_error_detail, load_library,
-    ns_batched, status_string, step_batched, workspace_bytes, KERNELS, timing_enable,
+    ns_batched, ns_batched_noalloc, NOALLOC_MAX_WORKSPACE, status_string, step_batched, workspace_bytes, KERNELS, timing_enable,
     timing_read, timing_reset, AdamWParams, adamw_batched, adamw_workspace_bytes, hbm_stream,
 )

@@ -17,12 +17,14 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "muon_mi355x.h")
 MUON_BF16, MUON_FP32 = 0, 1
 MUON_OK, MUON_ERR_INVALID_ARG, MUON_ERR_UNSUPPORTED, MUON_ERR_WORKSPACE, MUON_ERR_HIP = range(5)
 MAX_DIM = 65536
+NOALLOC_MAX_WORKSPACE = 256 << 20  # MUON_NOALLOC_MAX_WORKSPACE
 SIZE_MAX = ctypes.c_size_t(-1).value
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 CUBIC = (1.5, -0.5, 0.0)
 
-EXPORTED = ("muon_workspace_bytes", "muon_ns_batched", "muon_step_batched",
+EXPORTED = ("muon_workspace_bytes", "muon_ns_batched", "muon_ns_batched_noalloc",
+            "muon_step_batched",
             "muon_adamw_workspace_bytes", "muon_adamw_batched",
             "muon_status_string", "muon_last_error_detail", "muon_timing_enable",
             "muon_timing_read", "muon_timing_reset", "muon_hbm_stream")
@@ -73,6 +75,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_ns_batched.argtypes = [i32, i64p, i64p, vpp, vpp, i32, ctypes.POINTER(NsParams), vp,
                                     sz, vp]
     lib.muon_ns_batched.restype = i32
+    lib.muon_ns_batched_noalloc.argtypes = [i32, i64p, i64p, vpp, vpp, i32,
+                                            ctypes.POINTER(NsParams), vp]
+    lib.muon_ns_batched_noalloc.restype = i32
     lib.muon_step_batched.argtypes = [i32, i64p, i64p, vpp, vpp, vpp, i32,
                                       ctypes.POINTER(StepParams), vp, sz, vp]
     lib.muon_step_batched.restype = i32
@@ -208,6 +213,36 @@ def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
                                  ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                  ctypes.c_void_p(_stream_handle(dev)))
     _check(st, "muon_ns_batched")
+    return out
+
+
+def ns_batched_noalloc(xs: Sequence, out: Sequence, steps: int = 5, coeffs=QUINTIC,
+                       eps: float = 1e-7, cu_budget: int = 0) -> List:
+    """ns_batched through the allocation-free entry point: no workspace (the
+    library's own array of NOALLOC_MAX_WORKSPACE bytes per GPU serves), and the
+    caller passes the outputs.  Calls that overlap on one GPU race."""
+    import torch
+
+    lib = load_library()
+    xs, out = list(xs), list(out)
+    if not xs:
+        return out
+    if len(out) != len(xs):
+        raise ValueError("out must have one tensor per input")
+    dev = _check_tensors(out + xs, "xs/out")
+    shapes = [tuple(x.shape) for x in xs]
+    if any(tuple(o.shape) != s for o, s in zip(out, shapes)):
+        raise ValueError("out shapes must match the inputs")
+    a, b, c = (float(v) for v in coeffs)
+    p = NsParams(int(steps), a, b, c, float(eps), int(cu_budget))
+    with torch.cuda.device(dev):
+        st = lib.muon_ns_batched_noalloc(len(xs), _i64_array([s[0] for s in shapes]),
+                                         _i64_array([s[1] for s in shapes]),
+                                         _ptr_array([x.data_ptr() for x in xs]),
+                                         _ptr_array([o.data_ptr() for o in out]),
+                                         _dtype_code(xs[0].dtype), ctypes.byref(p),
+                                         ctypes.c_void_p(_stream_handle(dev)))
+    _check(st, "muon_ns_batched_noalloc")
     return out
 
 

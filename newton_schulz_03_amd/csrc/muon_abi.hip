@@ -347,12 +347,14 @@ hipEvent_t take_event() {
   return e;
 }
 
-// Brackets one launch with timing events when timing is enabled.
+// Brackets one launch with timing events when timing is enabled (and allowed:
+// the allocation-free entry point never creates events).
 struct TimedLaunch {
   int kernel;
   hipStream_t stream;
   hipEvent_t start = nullptr, stop = nullptr;
-  TimedLaunch(int k, hipStream_t s) : kernel(k), stream(s) {
+  TimedLaunch(int k, hipStream_t s, bool allowed = true) : kernel(k), stream(s) {
+    if (!allowed) return;
     std::lock_guard<std::mutex> lock(g_timing_mu);
     if (!g_timing_on) return;
     start = take_event();
@@ -407,7 +409,7 @@ int32_t check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
 
 // Enqueue the whole step after the table is in place.
 int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
-            const muon_ns_params& ns) {
+            const muon_ns_params& ns, bool timed = true) {
   LaunchCtx c;
   c.desc = reinterpret_cast<const MatDesc*>(ws);
   c.prefix = reinterpret_cast<const int32_t*>(ws + align_up(sizeof(MatDesc) * pl.batch, kAlign));
@@ -418,13 +420,13 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   c.stream = stream;
   hipError_t e;
   {
-    TimedLaunch t(MUON_K_PREPARE, stream);
+    TimedLaunch t(MUON_K_PREPARE, stream, timed);
     if ((e = launch_prepare(c, pl.totals[PH_PREPARE], pl.bf16, ep)) != hipSuccess)
       return hip_fail(e, "launch momentum/iterate/sum-of-squares");
     t.done();
   }
   {
-    TimedLaunch t(MUON_K_NORM, stream);
+    TimedLaunch t(MUON_K_NORM, stream, timed);
     if ((e = launch_finalize(c, ep)) != hipSuccess) return hip_fail(e, "launch norm finalize");
     t.done();
   }
@@ -434,21 +436,22 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   int32_t cur = 0;
   for (int k = 0; k < ns.steps; ++k) {
     {
-      TimedLaunch t(MUON_K_GRAM, stream);
+      TimedLaunch t(MUON_K_GRAM, stream, timed);
       if ((e = launch_gram(c, pl.split_gram, pl.bf16, cur, use_poly ? 1.f : ns.b, k == 0)) !=
           hipSuccess)
         return hip_fail(e, "launch Gram");
       t.done();
     }
     if (use_poly) {
-      TimedLaunch t(MUON_K_POLY, stream);
+      TimedLaunch t(MUON_K_POLY, stream, timed);
       if ((e = launch_poly(c, pl.split_poly, pl.bf16, ns.b, ns.c)) != hipSuccess)
         return hip_fail(e, "launch polynomial");
       t.done();
     }
     const bool last = fused && k + 1 == ns.steps;
     {
-      TimedLaunch t(last ? MUON_K_PROD_FINISH : k == 0 ? MUON_K_PROD_FIRST : MUON_K_PROD, stream);
+      TimedLaunch t(last ? MUON_K_PROD_FINISH : k == 0 ? MUON_K_PROD_FIRST : MUON_K_PROD, stream,
+                    timed);
       const int32_t fin = !last ? FIN_NONE : ep.mode == MODE_STEP ? FIN_STEP : FIN_NS;
       // wide tiles for the products that store the iterate, unless a CU budget
       // asks for the looping launches (256-wide tiles only)
@@ -468,7 +471,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   fp.cur = cur;
   fp.scale_x = ns.steps == 0 ? 1 : 0;  // no product took the norm factor
   {
-    TimedLaunch t(MUON_K_FINISH, stream);
+    TimedLaunch t(MUON_K_FINISH, stream, timed);
     if ((e = launch_finish(c, pl.totals[PH_FINISH], pl.bf16, fp)) != hipSuccess)
       return hip_fail(e, "launch finish");
     t.done();
@@ -488,6 +491,45 @@ extern "C" size_t muon_workspace_bytes(int32_t batch, const int64_t* rows, const
   return pl.total_bytes;
 }
 
+namespace muon {
+namespace {
+
+// Validation of the orthogonalize-only call's pointer arguments.
+int32_t check_ns_pointers(int32_t batch, const void* const* x, void* const* out) {
+  if (x == nullptr || out == nullptr) return fail(MUON_ERR_INVALID_ARG, "x/out array is null");
+  for (int32_t i = 0; i < batch; ++i) {
+    if (x[i] == nullptr || out[i] == nullptr)
+      return fail(MUON_ERR_INVALID_ARG, "matrix %d: null device pointer", i);
+    if (!aligned16(x[i]) || !aligned16(out[i]))
+      return fail(MUON_ERR_INVALID_ARG, "matrix %d: device pointer not 16-byte aligned", i);
+  }
+  return MUON_OK;
+}
+
+void bind_ns(Plan& pl, char* ws, const void* const* x, void* const* out) {
+  bind(pl, ws);
+  for (int32_t i = 0; i < pl.batch; ++i) {
+    pl.desc[i].src = x[i];
+    pl.desc[i].mom = nullptr;
+    pl.desc[i].dst = out[i];
+  }
+}
+
+// The allocation-free variant of the orthogonalize-only call takes its
+// workspace from the library's scratch array (noalloc_scratch.hip) and sends
+// the descriptor table as kernel arguments.
+int32_t put_table(const Plan& pl, char* ws, hipStream_t stream) {
+  const size_t desc_bytes = sizeof(MatDesc) * pl.batch;
+  hipError_t e = launch_put_bytes(pl.desc.data(), desc_bytes, ws, stream);
+  if (e == hipSuccess)
+    e = launch_put_bytes(pl.prefix.data(), sizeof(int32_t) * pl.prefix.size(),
+                         ws + align_up(desc_bytes, kAlign), stream);
+  return e == hipSuccess ? MUON_OK : hip_fail(e, "launch descriptor copy");
+}
+
+}  // namespace
+}  // namespace muon
+
 extern "C" int32_t muon_ns_batched(int32_t batch, const int64_t* rows, const int64_t* cols,
                                    const void* const* x, void* const* out, int32_t dtype,
                                    const muon_ns_params* p, void* workspace,
@@ -499,27 +541,46 @@ extern "C" int32_t muon_ns_batched(int32_t batch, const int64_t* rows, const int
     if (st != MUON_OK) return st;
     if ((st = check_ns_params(p)) != MUON_OK) return st;
     if (batch == 0) return MUON_OK;
-    if (x == nullptr || out == nullptr) return fail(MUON_ERR_INVALID_ARG, "x/out array is null");
-    for (int32_t i = 0; i < batch; ++i) {
-      if (x[i] == nullptr || out[i] == nullptr)
-        return fail(MUON_ERR_INVALID_ARG, "matrix %d: null device pointer", i);
-      if (!aligned16(x[i]) || !aligned16(out[i]))
-        return fail(MUON_ERR_INVALID_ARG, "matrix %d: device pointer not 16-byte aligned", i);
-    }
+    if ((st = check_ns_pointers(batch, x, out)) != MUON_OK) return st;
     if ((st = check_ws(pl, workspace, workspace_bytes)) != MUON_OK) return st;
     char* ws = static_cast<char*>(workspace);
-    bind(pl, ws);
-    for (int32_t i = 0; i < batch; ++i) {
-      pl.desc[i].src = x[i];
-      pl.desc[i].mom = nullptr;
-      pl.desc[i].dst = out[i];
-    }
+    bind_ns(pl, ws, x, out);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = upload_table(pl, ws, s)) != MUON_OK) return st;
     ElemParams ep{};
     ep.mode = MODE_NS;
     ep.eps = p->eps;
     return run(pl, ws, s, ep, *p);
+  } catch (...) {
+    return fail(MUON_ERR_HIP, "unexpected host exception");
+  }
+}
+
+extern "C" int32_t muon_ns_batched_noalloc(int32_t batch, const int64_t* rows, const int64_t* cols,
+                                           const void* const* x, void* const* out, int32_t dtype,
+                                           const muon_ns_params* p, void* stream) {
+  try {
+    g_detail.clear();
+    Plan pl;
+    int32_t st = make_plan(batch, rows, cols, dtype, pl);
+    if (st != MUON_OK) return st;
+    if ((st = check_ns_params(p)) != MUON_OK) return st;
+    if (batch == 0) return MUON_OK;
+    if ((st = check_ns_pointers(batch, x, out)) != MUON_OK) return st;
+    if (pl.total_bytes > MUON_NOALLOC_MAX_WORKSPACE)
+      return fail(MUON_ERR_WORKSPACE,
+                  "the batch needs %zu bytes of workspace; the allocation-free call has %zu",
+                  pl.total_bytes, static_cast<size_t>(MUON_NOALLOC_MAX_WORKSPACE));
+    char* ws = nullptr;
+    const hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (the scratch array)");
+    bind_ns(pl, ws, x, out);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = put_table(pl, ws, s)) != MUON_OK) return st;
+    ElemParams ep{};
+    ep.mode = MODE_NS;
+    ep.eps = p->eps;
+    return run(pl, ws, s, ep, *p, /*timed=*/false);
   } catch (...) {
     return fail(MUON_ERR_HIP, "unexpected host exception");
   }

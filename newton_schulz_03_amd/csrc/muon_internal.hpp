@@ -133,4 +133,12 @@ hipError_t launch_prod(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int
 hipError_t launch_prod_wide(const LaunchCtx& c, const XcdSplit& sp, int32_t cur, float a,
                             bool use_poly, bool first);
 
+// The allocation-free entry point (noalloc_scratch.hip).  noalloc_scratch:
+// the device address of the library's scratch array on the current device
+// (MUON_NOALLOC_MAX_WORKSPACE bytes, looked up once per device).
+// launch_put_bytes: enqueues kernels on `s` that write the n host bytes at
+// src to dst, carrying them as kernel arguments (no staging memory).
+hipError_t noalloc_scratch(char** base);
+hipError_t launch_put_bytes(const void* src, size_t n, void* dst, hipStream_t s);
+
 }  // namespace muon

@@ -202,3 +202,28 @@ def test_hbm_stream_validation(lib):
         st = lib.muon_hbm_stream(n_in, args[0], n_out, args[1], nbytes, 0, None)
         assert st == nsa.MUON_ERR_INVALID_ARG, (n_in, n_out, nbytes)
     assert lib.muon_hbm_stream(2, ins, 2, outs, 0, 1, None) == nsa.MUON_OK
+
+
+def test_ns_noalloc_validation(lib):
+    """The allocation-free call validates like muon_ns_batched, and refuses a batch
+    whose workspace exceeds the library's array (MUON_NOALLOC_MAX_WORKSPACE)
+    before any HIP call."""
+    p = NsParams(5, 3.4445, -4.775, 2.0315, 1e-7, 0)
+    ptrs = _ptr_array([FAKE])
+    assert lib.muon_ns_batched_noalloc(0, None, None, None, None, 0, ctypes.byref(p), None) == \
+        nsa.MUON_OK
+    st = lib.muon_ns_batched_noalloc(1, _i64_array([64]), _i64_array([96]), None, ptrs, 0,
+                                     ctypes.byref(p), None)
+    assert st == nsa.MUON_ERR_INVALID_ARG
+    st = lib.muon_ns_batched_noalloc(1, _i64_array([64]), _i64_array([96]), _ptr_array([FAKE + 8]),
+                                     ptrs, 0, ctypes.byref(p), None)
+    assert st == nsa.MUON_ERR_INVALID_ARG
+    bad = NsParams(-1, 3.4445, -4.775, 2.0315, 1e-7, 0)
+    st = lib.muon_ns_batched_noalloc(1, _i64_array([64]), _i64_array([96]), ptrs, ptrs, 0,
+                                     ctypes.byref(bad), None)
+    assert st == nsa.MUON_ERR_INVALID_ARG
+    big = 8192  # bf16 workspace 2 * 8192^2 * 2 * 2 bytes = 512 MiB
+    assert nsa.workspace_bytes([(big, big)], nsa.MUON_BF16) > nsa.NOALLOC_MAX_WORKSPACE
+    st = lib.muon_ns_batched_noalloc(1, _i64_array([big]), _i64_array([big]), ptrs, ptrs, 0,
+                                     ctypes.byref(p), None)
+    assert st == nsa.MUON_ERR_WORKSPACE and "allocation-free" in nsa.last_error_detail()
