@@ -3,19 +3,31 @@
 The pages list FP8 for expert matrix math as an open question ("Domyn is
 training a 1T-parameter MoE on Europe's Jupiter supercomputer, and published
 the recipe", §What moved the number, closing paragraph).  This emulation
-rounds the operands of the products to e4m3 (torch's float8_e4m3fn cast,
-round to nearest even), accumulates in float32 and stores in bf16, as a
-matrix-core FP8 kernel would, and compares with the float64 oracle.
+quantizes the operands of the products to e4m3 with one power-of-two scale
+per 32 consecutive elements along the contracted dimension (the block-scaled
+form gfx950's scaled matrix-core instructions consume), forms the products
+exactly (as an fp32-accumulating matrix core would, up to accumulation order)
+and stores every result in bf16, as the bf16 path does; the additive terms
+(b A, a X) stay in bf16.  It compares with the float64 oracle.
 
-What it pins:
+What it pins (measured on Gaussian inputs, 5 quintic steps):
 
-- **All three products in e4m3 break the iteration.** X' = aX + BX cancels
-  heavily, so 3% element error in B is amplified. The output leaves the
-  quintic's singular-value band.
-- **Only the Gram in e4m3 keeps the band**, at a few percent error: 3-4 times
-  the bf16 path's error.
+- **e4m3 in every product of every step breaks the iteration**: 25-43% error,
+  singular values out of the quintic band.  X' = aX + BX cancels heavily
+  (a = 3.4445 against B near -2.7 I), so the few-percent element error of e4m3
+  is amplified.
+- **e4m3 in every product of the first two steps only** (bf16 in the last
+  three) is as accurate as the bf16 path on every shape tried (2048x6144,
+  6144x2048, 1024x3072, 6144x1024, 512x1536: 0.90e-2 to 0.94e-2 against
+  0.91e-2 to 1.17e-2 for bf16).  In the first steps the singular values are
+  small and the polynomial is nearly linear, so the element noise enters as a
+  small relative perturbation that the later bf16 steps do not amplify.
+- **Three e4m3 steps hold only on large matrices**: 1.1e-2 on the expert
+  shape 2048x6144, but 2.1e-2 at 6144x1024 and 2.9e-2 to 3.6e-2 at 1024x3072.
+- The scale granularity hardly matters: one scale per 32 elements, per row or
+  per tensor give errors within 3% of each other on these inputs.
 
-No FP8 kernel is built on that account.
+Hence the FP8 mode of the library: e4m3 products in the first two steps.
 """
 import numpy as np
 import pytest
@@ -25,52 +37,91 @@ import oracle
 
 pytestmark = pytest.mark.slow
 
-
-def q8(a, scale):
-    t = torch.from_numpy(np.asarray(a * scale, np.float32)).to(torch.float8_e4m3fn)
-    return t.to(torch.float32).numpy().astype(np.float64) / scale
+E4M3_MAX = 448.0
 
 
 def bf(a):
     return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
 
 
-def ns_emulated(u, fp8_products, steps=5, coeffs=oracle.QUINTIC):
+def mx_e4m3(a, axis):
+    """e4m3 values with one power-of-two scale per 32 consecutive elements along
+    `axis`: the smallest power of two that brings the block maximum to at most
+    448 (e4m3's largest value, so nothing saturates), then each element rounded
+    to nearest even by torch's float8_e4m3fn cast.  Returns the exact values."""
+    a = np.moveaxis(np.asarray(a, np.float64), axis, -1)
+    n = a.shape[-1]
+    pad = (-n) % 32
+    if pad:
+        a = np.concatenate([a, np.zeros(a.shape[:-1] + (pad,))], -1)
+    b = a.reshape(a.shape[:-1] + (-1, 32))
+    amax = np.abs(b).max(-1, keepdims=True)
+    e = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX)), 0)
+    s = 2.0 ** e
+    q = b / s
+    q = torch.from_numpy(q.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return np.moveaxis((q * s).reshape(a.shape)[..., :n], -1, axis)
+
+
+def ns_emulated(u, fp8_steps, fp8_products=("gram", "square", "product"), steps=5,
+                coeffs=oracle.QUINTIC):
+    """bf16 Newton-Schulz with e4m3 operands in `fp8_products` of the first
+    `fp8_steps` steps (A = X X^T contracts along the long side, A^2 and B X
+    along the short side)."""
     a, b, c = coeffs
-    x = u.T if u.shape[0] > u.shape[1] else u
+    tall = u.shape[0] > u.shape[1]
+    x = u.T if tall else u
     x = bf(x / (np.linalg.norm(x) + 1e-7))
-    # power-of-two scale that brings the iterate's entries (about 1/sqrt(l)) to about 1
-    sx = 2.0 ** np.round(np.log2(np.sqrt(x.shape[1])))
-    for _ in range(steps):
-        xg = q8(x, sx) if "gram" in fp8_products else x
+    for k in range(steps):
+        f8 = k < fp8_steps
+        xg = mx_e4m3(x, 1) if f8 and "gram" in fp8_products else x
         A = bf(xg @ xg.T)
-        Ap = q8(A, 1.0) if "square" in fp8_products else A
-        B = bf(b * A + c * (Ap @ Ap))
-        if "product" in fp8_products:
-            x = bf(a * x + q8(B, 1.0) @ q8(x, sx))
+        aq = mx_e4m3(A, 1) if f8 and "square" in fp8_products else A
+        B = bf(c * (aq @ aq.T) + b * A)
+        if f8 and "product" in fp8_products:
+            x = bf(a * x + mx_e4m3(B, 1) @ mx_e4m3(x, 0))
         else:
             x = bf(a * x + B @ x)
-    return x.T if u.shape[0] > u.shape[1] else x
+    return x.T if tall else x
 
 
-def run(shape, products, seed=0):
+def run(shape, fp8_steps, seed=0, **kw):
     u = np.random.default_rng(seed).standard_normal(shape)
     ref = oracle.newton_schulz(u, 5)
-    o = ns_emulated(u, products)
+    o = ns_emulated(u, fp8_steps, **kw)
     err = np.linalg.norm(o - ref) / np.linalg.norm(ref)
     sv = np.linalg.svd(o, compute_uv=False)
     return err, sv
 
 
+def test_block_scaling_is_exact_for_powers_of_two_and_bounded_elsewhere():
+    """The quantizer keeps values that e4m3 holds exactly (a block of powers of
+    two), and errs by at most 2^-4 relative in the normal range."""
+    # block maximum 2^11: scale 2^3 (2^11 / 2^3 = 256 <= 448 < 512), so the block
+    # holds 2^3 times e4m3's powers of two, 2^-9 (smallest subnormal) to 2^8;
+    # 2^-7 and below round to zero
+    x = 2.0 ** np.arange(-20, 12, dtype=np.float64).reshape(1, 32)
+    assert np.array_equal(mx_e4m3(x, 1), np.where(x >= 2.0 ** -6, x, 0.0))
+    rng = np.random.default_rng(3)
+    y = rng.uniform(1.0, 2.0, size=(64, 64))
+    rel = np.abs(mx_e4m3(y, 1) - y) / y
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+
+
 @pytest.mark.parametrize("shape", [(256, 768), (512, 1024)])
-def test_fp8_in_every_product_breaks_the_band(shape):
-    err, sv = run(shape, {"gram", "square", "product"})
+def test_fp8_in_every_step_breaks_the_band(shape):
+    err, sv = run(shape, fp8_steps=5)
     assert err > 0.1 and (sv.max() > 1.25 or sv.min() < 0.6), (err, sv.min(), sv.max())
 
 
-@pytest.mark.parametrize("shape", [(256, 768), (512, 1024)])
-def test_fp8_gram_only_keeps_the_band(shape):
-    err, sv = run(shape, {"gram"})
-    bf16_err, _ = run(shape, set())
-    assert 0.6 <= sv.min() and sv.max() <= 1.25, (sv.min(), sv.max())
-    assert err < 0.08 and err > 2 * bf16_err, (err, bf16_err)
+@pytest.mark.parametrize("shape", [(512, 1536), (1536, 512), (1024, 3072)])
+def test_fp8_in_the_first_two_steps_matches_bf16(shape):
+    err, sv = run(shape, fp8_steps=2)
+    bf16_err, _ = run(shape, fp8_steps=0)
+    assert err <= 1.1 * bf16_err and err <= 2e-2, (err, bf16_err)
+    assert 0.6818 - 2e-2 <= sv.min() and sv.max() <= 1.1344 + 2e-2, (sv.min(), sv.max())
+
+
+def test_three_fp8_steps_exceed_the_tolerance_on_smaller_matrices():
+    err, _ = run((1024, 3072), fp8_steps=3)
+    assert err > 2e-2, err
