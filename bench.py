@@ -37,7 +37,7 @@ METRIC = "expert matrices orthogonalized/sec + % bf16 MFMA peak (6144×2048, 5 N
 # WRITE_SIZE, scaled by a copy of known size); used while the kernel sources are unchanged
 TRAFFIC_WORKLOAD = "c2_96x2048x6144"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_prod_c2_96x2048x6144.md")
-PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # dense matrix-core peaks at 2.4 GHz
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3, "e4m3": 5033.2}  # dense matrix-core peaks, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
 
@@ -415,6 +415,9 @@ def main(argv=None) -> int:
                     help="CUs the dense orthogonalization keeps in the budgeted overlap runs")
     ap.add_argument("--overlap-copies", type=int, default=100,
                     help="1 GiB device copies in the bandwidth-bound overlap load")
+    ap.add_argument("--fp8-steps", type=int, default=0,
+                    help="e4m3 operands in the first N Newton-Schulz steps (bf16 workloads; "
+                         "the line is then labelled as such, not the bf16 headline)")
     ap.add_argument("--momentum-host", action="store_true",
                     help="keep the momentum in pinned host memory (the GPU reads and writes it "
                          "in place over the host link)")
@@ -459,7 +462,7 @@ def main(argv=None) -> int:
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     shapes = list(wl.shapes)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    ws = nsa.allocate_workspace(shapes, tdt, dev)
+    ws = nsa.allocate_workspace(shapes, tdt, dev, fp8=args.fp8_steps > 0)
     c = wl.coeffs[2]
 
     if wl.call == "step":
@@ -476,13 +479,14 @@ def main(argv=None) -> int:
         def step():
             nsa.step_batched(W, G, M, lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov,
                              steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps, workspace=ws,
-                             momentum_host=args.momentum_host)
+                             momentum_host=args.momentum_host, fp8_steps=args.fp8_steps)
     else:
         X = [d["x"] for d in ins]
         OUT = [torch.empty_like(x) for x in X]
 
         def step():
-            nsa.ns_batched(X, steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps, out=OUT, workspace=ws)
+            nsa.ns_batched(X, steps=wl.steps, coeffs=wl.coeffs, eps=wl.eps, out=OUT, workspace=ws,
+                           fp8_steps=args.fp8_steps)
 
     for _ in range(args.warmup):
         step()
@@ -533,7 +537,8 @@ def main(argv=None) -> int:
     achieved = alg_prod_launch / (prod_ms * 1e-3) / 1e12
     per_kernel = {k: {"avg_ms": round(avg(k), 4), "launches": kern[k][1]} for k in nsa.KERNELS
                   if kern[k][1]}
-    ns_ms = sum(kern[k][0] for k in ("gram", "poly", "prod_first", "prod", "prod_finish")) / args.steps
+    ns_ms = sum(kern[k][0] for k in ("gram", "poly", "prod_first", "prod", "prod_finish", "quant8",
+                                     "gram8", "poly8", "prod8")) / args.steps
     ew = [elementwise_bytes(s, esize, wl.call) for s in shapes]
     for name, idx in (("prepare", 0), ("finish", 1)):
         if name not in per_kernel:
@@ -542,15 +547,19 @@ def main(argv=None) -> int:
         per_kernel[name]["gbs"] = round(b / (avg(name) * 1e-3) / 1e9, 1)
         per_kernel[name]["hbm_frac"] = round(b / (avg(name) * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)
     for name, flops in (("gram", alg_gram_launch), ("poly", alg_poly_launch), ("prod", alg_prod_launch),
-                        ("prod_first", alg_prod_launch)):
+                        ("prod_first", alg_prod_launch), ("gram8", alg_gram_launch),
+                        ("poly8", alg_poly_launch), ("prod8", alg_prod_launch)):
         if kern[name][1]:
             t = flops / (avg(name) * 1e-3) / 1e12
             per_kernel[name]["tflops"] = round(t, 1)
-            per_kernel[name]["mfma_frac"] = round(t / peak, 3)
+            per_kernel[name]["mfma_frac"] = round(t / (PEAK_TFLOPS["e4m3"] if name.endswith("8")
+                                                       else peak), 3)
 
     value = wl.batch * args.steps / (total_ms * 1e-3)
+    metric = METRIC if args.fp8_steps == 0 else (
+        METRIC + f" [e4m3 operands in the first {args.fp8_steps} NS steps]")
     result = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "matrices/s",
         "n_gpus": 1,
@@ -560,12 +569,13 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": wl.dtype if args.fp8_steps == 0 else wl.dtype + "+e4m3",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "shapes": sorted({tuple(s) for s in shapes}),
                    "ns_steps": wl.steps, "coeffs": list(wl.coeffs), "call": wl.call,
                    "nesterov": wl.nesterov, "lr": wl.lr, "beta": wl.beta,
-                   "momentum": "pinned host memory" if args.momentum_host else "HBM"},
+                   "momentum": "pinned host memory" if args.momentum_host else "HBM",
+                   "fp8_steps": args.fp8_steps},
         "roofline": {"bound": "mfma", "kernel": "prod (X <- aX + BX)", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": rocprof_summary.read_traffic(TRAFFIC_SUMMARY, wl.name)

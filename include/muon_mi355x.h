@@ -100,6 +100,20 @@ typedef struct {
    * multiple of 384), with N > 0 tiles of 256 x 256, and both add up every
    * element the same way. */
   int32_t cu_budget;
+  /* e4m3 operands in the first fp8_steps iterations (0: none; bf16 only,
+   * 0 <= fp8_steps < steps, no cu_budget).  FP8 for expert matrix math is an
+   * open question on "Domyn is training a 1T-parameter MoE on Europe's Jupiter
+   * supercomputer, and published the recipe" (§What moved the number, closing
+   * paragraph).  In those iterations the three products take e4m3 operands
+   * with one power-of-two scale per 32 elements along the contracted side
+   * (the block maximum at most 448), formed from the bf16 X, A and B; the
+   * products accumulate in fp32, the a X and b A terms are added in fp32 from
+   * the bf16 matrices, and every result is stored in bf16 as before.  With
+   * fp8_steps = 2 of 5 the output is as close to the exact iteration as the
+   * bf16 path's; more e4m3 steps are not (the polynomial amplifies their
+   * noise once the singular values have grown).  Such a call needs
+   * muon_workspace_bytes_fp8() bytes of workspace. */
+  int32_t fp8_steps;
 } muon_ns_params;
 
 /*
@@ -129,6 +143,14 @@ typedef struct {
  * batch == 0 returns 0.  Host-only: launches nothing, needs no GPU.
  */
 size_t muon_workspace_bytes(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype);
+
+/*
+ * Bytes of device workspace a bf16 call with fp8_steps > 0 needs over this
+ * batch: muon_workspace_bytes() plus two e4m3 copies of each padded iterate
+ * (s_pad * l_pad bytes each, plus a scale byte per 32).  Returns SIZE_MAX on
+ * invalid arguments.  Host-only.
+ */
+size_t muon_workspace_bytes_fp8(int32_t batch, const int64_t* rows, const int64_t* cols);
 
 /*
  * Orthogonalize a ragged batch: out[i] = NS_k(x[i]) (shape rows[i] x cols[i]).
@@ -237,7 +259,11 @@ typedef enum {
   MUON_K_ADAMW = 6,     /* muon_adamw_batched */
   MUON_K_PROD_FINISH = 7, /* bf16: the last X <- a X + B X, writing W (or the output) itself */
   MUON_K_PROD_FIRST = 8,  /* the first X <- a X + B X (its iterate is U, scaled as it is stored) */
-  MUON_K_COUNT = 9
+  MUON_K_QUANT8 = 9,      /* e4m3 steps: the block-scaled e4m3 copies of X, A and B */
+  MUON_K_GRAM8 = 10,      /* e4m3 steps: A = X X^T */
+  MUON_K_POLY8 = 11,      /* e4m3 steps: B = b A + c A^2 */
+  MUON_K_PROD8 = 12,      /* e4m3 steps: X <- a X + B X */
+  MUON_K_COUNT = 13
 } muon_kernel;
 
 /*

@@ -23,12 +23,14 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 QUINTIC = (3.4445, -4.7750, 2.0315)
 CUBIC = (1.5, -0.5, 0.0)
 
-EXPORTED = ("muon_workspace_bytes", "muon_ns_batched", "muon_ns_batched_noalloc",
+EXPORTED = ("muon_workspace_bytes", "muon_workspace_bytes_fp8", "muon_ns_batched",
+            "muon_ns_batched_noalloc",
             "muon_step_batched",
             "muon_adamw_workspace_bytes", "muon_adamw_batched",
             "muon_status_string", "muon_last_error_detail", "muon_timing_enable",
             "muon_timing_read", "muon_timing_reset", "muon_hbm_stream")
-KERNELS = ("prepare", "norm", "gram", "poly", "prod", "finish", "adamw", "prod_finish", "prod_first")
+KERNELS = ("prepare", "norm", "gram", "poly", "prod", "finish", "adamw", "prod_finish", "prod_first",
+           "quant8", "gram8", "poly8", "prod8")
 
 
 class MuonError(RuntimeError):
@@ -41,7 +43,8 @@ class MuonError(RuntimeError):
 
 class NsParams(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
-                ("c", ctypes.c_float), ("eps", ctypes.c_float), ("cu_budget", ctypes.c_int32)]
+                ("c", ctypes.c_float), ("eps", ctypes.c_float), ("cu_budget", ctypes.c_int32),
+                ("fp8_steps", ctypes.c_int32)]
 
 
 class StepParams(ctypes.Structure):
@@ -72,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_size_t)
     lib.muon_workspace_bytes.argtypes = [i32, i64p, i64p, i32]
     lib.muon_workspace_bytes.restype = sz
+    lib.muon_workspace_bytes_fp8.argtypes = [i32, i64p, i64p]
+    lib.muon_workspace_bytes_fp8.restype = sz
     lib.muon_ns_batched.argtypes = [i32, i64p, i64p, vpp, vpp, i32, ctypes.POINTER(NsParams), vp,
                                     sz, vp]
     lib.muon_ns_batched.restype = i32
@@ -134,23 +139,28 @@ def _dtype_code(dtype) -> int:
     raise TypeError(f"unsupported dtype {dtype}: use torch.bfloat16 or torch.float32")
 
 
-def workspace_bytes(shapes: Sequence[Tuple[int, int]], dtype) -> int:
-    """Device workspace bytes for a batch of (rows, cols) shapes."""
+def workspace_bytes(shapes: Sequence[Tuple[int, int]], dtype, fp8: bool = False) -> int:
+    """Device workspace bytes for a batch of (rows, cols) shapes (fp8: for a bf16
+    call with e4m3 steps)."""
     lib = load_library()
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     rows = _i64_array([int(r) for r, _ in shapes])
     cols = _i64_array([int(c) for _, c in shapes])
-    n = lib.muon_workspace_bytes(len(shapes), rows, cols, code)
+    if fp8:
+        n = lib.muon_workspace_bytes_fp8(len(shapes), rows, cols)
+    else:
+        n = lib.muon_workspace_bytes(len(shapes), rows, cols, code)
     if n == SIZE_MAX:
         raise MuonError(MUON_ERR_INVALID_ARG, "muon_workspace_bytes", last_error_detail())
     return int(n)
 
 
-def allocate_workspace(shapes, dtype, device):
-    """A uint8 device tensor usable as the workspace of a call over `shapes`."""
+def allocate_workspace(shapes, dtype, device, fp8: bool = False):
+    """A uint8 device tensor usable as the workspace of a call over `shapes`
+    (fp8: with e4m3 steps)."""
     import torch
 
-    n = workspace_bytes(shapes, dtype)
+    n = workspace_bytes(shapes, dtype, fp8)
     ws = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + max(n, 1)]
@@ -177,12 +187,15 @@ def _check_tensors(ts, name):
 
 
 def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
-               out: Optional[Sequence] = None, workspace=None, cu_budget: int = 0) -> List:
+               out: Optional[Sequence] = None, workspace=None, cu_budget: int = 0,
+               fp8_steps: int = 0) -> List:
     """Newton-Schulz orthogonalization of a ragged batch of matrices on the GPU.
 
     Returns the outputs (new tensors, or `out` when given; out[i] may be xs[i]).
     Runs on the current HIP stream of the tensors' device.  cu_budget > 0 keeps
-    the matrix-core launches to that many CUs (the rest stay free for other streams).
+    the matrix-core launches to that many CUs (the rest stay free for other
+    streams).  fp8_steps > 0 (bf16, fewer than steps): the first fp8_steps
+    iterations take block-scaled e4m3 operands.
     """
     import torch
 
@@ -202,9 +215,9 @@ def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
         raise ValueError("out shapes must match the inputs")
     code = _dtype_code(xs[0].dtype)
     if workspace is None:
-        workspace = allocate_workspace(shapes, xs[0].dtype, dev)
+        workspace = allocate_workspace(shapes, xs[0].dtype, dev, fp8=fp8_steps > 0)
     a, b, c = (float(v) for v in coeffs)
-    p = NsParams(int(steps), a, b, c, float(eps), int(cu_budget))
+    p = NsParams(int(steps), a, b, c, float(eps), int(cu_budget), int(fp8_steps))
     with torch.cuda.device(dev):
         st = lib.muon_ns_batched(len(xs), _i64_array([s[0] for s in shapes]),
                                  _i64_array([s[1] for s in shapes]),
@@ -217,7 +230,7 @@ def ns_batched(xs: Sequence, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
 
 
 def ns_batched_noalloc(xs: Sequence, out: Sequence, steps: int = 5, coeffs=QUINTIC,
-                       eps: float = 1e-7, cu_budget: int = 0) -> List:
+                       eps: float = 1e-7, cu_budget: int = 0, fp8_steps: int = 0) -> List:
     """ns_batched through the allocation-free entry point: no workspace (the
     library's own array of NOALLOC_MAX_WORKSPACE bytes per GPU serves), and the
     caller passes the outputs.  Calls that overlap on one GPU race."""
@@ -234,7 +247,7 @@ def ns_batched_noalloc(xs: Sequence, out: Sequence, steps: int = 5, coeffs=QUINT
     if any(tuple(o.shape) != s for o, s in zip(out, shapes)):
         raise ValueError("out shapes must match the inputs")
     a, b, c = (float(v) for v in coeffs)
-    p = NsParams(int(steps), a, b, c, float(eps), int(cu_budget))
+    p = NsParams(int(steps), a, b, c, float(eps), int(cu_budget), int(fp8_steps))
     with torch.cuda.device(dev):
         st = lib.muon_ns_batched_noalloc(len(xs), _i64_array([s[0] for s in shapes]),
                                          _i64_array([s[1] for s in shapes]),
@@ -248,7 +261,8 @@ def ns_batched_noalloc(xs: Sequence, out: Sequence, steps: int = 5, coeffs=QUINT
 
 def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, beta: float = 0.95,
                  nesterov: bool = False, steps: int = 5, coeffs=QUINTIC, eps: float = 1e-7,
-                 workspace=None, momentum_host: bool = False, cu_budget: int = 0) -> None:
+                 workspace=None, momentum_host: bool = False, cu_budget: int = 0,
+                 fp8_steps: int = 0) -> None:
     """One Muon step over a ragged batch, in place on ws (weights) and ms (momentum).
 
     momentum_host: the momenta are pinned host tensors (pin_memory), which the
@@ -276,10 +290,10 @@ def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, bet
         raise ValueError("w, g and m of one matrix must share a shape")
     code = _dtype_code(ws[0].dtype)
     if workspace is None:
-        workspace = allocate_workspace(shapes, ws[0].dtype, dev)
+        workspace = allocate_workspace(shapes, ws[0].dtype, dev, fp8=fp8_steps > 0)
     a, b, c = (float(v) for v in coeffs)
     p = StepParams(float(lr), float(beta), 1 if nesterov else 0,
-                   NsParams(int(steps), a, b, c, float(eps), int(cu_budget)),
+                   NsParams(int(steps), a, b, c, float(eps), int(cu_budget), int(fp8_steps)),
                    1 if momentum_host else 0)
     with torch.cuda.device(dev):
         st = lib.muon_step_batched(len(ws), _i64_array([s[0] for s in shapes]),

@@ -41,12 +41,13 @@ struct Plan {
   std::vector<MatDesc> desc;        // workspace pointers filled in by bind()
   std::vector<size_t> mat_off;      // byte offset of matrix i's buffers
   std::vector<int32_t> prefix;      // NPHASE x (batch + 1)
-  int32_t totals[NPHASE] = {0, 0, 0, 0, 0};
+  int32_t totals[NPHASE] = {};
   XcdSplit split_gram{}, split_poly{}, split_prod{};  // matrix-core launches over the XCDs
   // Wide product tiles (256 x kTileW): every matrix's padded long side is a
   // multiple of kTileW.  Then the products that store the iterate use them.
   bool wide_prod = false;
   XcdSplit split_prodw{};
+  bool fp8 = false;                 // the workspace holds the e4m3 buffers (f8)
   size_t table_bytes = 0;
   size_t inv_off = 0;
   size_t partials_off = 0;
@@ -88,8 +89,10 @@ int32_t make_split(const std::vector<int64_t>& cnt, const std::vector<int64_t>& 
   return MUON_OK;
 }
 
-// Shapes and counts only; no pointers.  Returns MUON_OK or an error (with detail).
-int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype, Plan& pl) {
+// Shapes and counts only; no pointers.  fp8: the workspace also holds the
+// e4m3 buffers of the e4m3 steps.  Returns MUON_OK or an error (with detail).
+int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype, Plan& pl,
+                  bool fp8 = false) {
   if (batch < 0) return fail(MUON_ERR_INVALID_ARG, "batch = %d is negative", batch);
   if (dtype != MUON_BF16 && dtype != MUON_FP32)
     return fail(MUON_ERR_INVALID_ARG, "unknown dtype %d", dtype);
@@ -97,12 +100,13 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
     return fail(MUON_ERR_INVALID_ARG, "rows/cols array is null");
   pl.batch = batch;
   pl.bf16 = dtype == MUON_BF16;
+  pl.fp8 = fp8;
   pl.esize = pl.bf16 ? 2 : 4;
   const int64_t vec = 16 / static_cast<int64_t>(pl.esize);
   pl.desc.assign(batch, MatDesc{});
   pl.mat_off.assign(batch, 0);
   pl.prefix.assign(static_cast<size_t>(NPHASE) * (batch + 1), 0);
-  int64_t tot[NPHASE] = {0, 0, 0, 0, 0};
+  int64_t tot[NPHASE] = {};
   // per matrix: symmetric and product tiles; K slices of the Gram (long side)
   // and of A^2 and the product (short side)
   std::vector<int64_t> sym_cnt(batch), prod_cnt(batch), prodw_cnt(batch), k_long(batch),
@@ -135,6 +139,8 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
         ts * tl,                                                             // PH_PROD
         cdiv(r, kEwTile) * cdiv(c, kEwTile),                                 // PH_FINISH
         d.l_pad % kTileW == 0 ? ts * (d.l_pad / kTileW) : 0,                 // PH_PRODW
+        static_cast<int64_t>(d.s_pad / kQ8Tile) * (d.l_pad / kQ8Tile),       // PH_Q8X
+        static_cast<int64_t>(d.s_pad / kQ8Tile) * (d.s_pad / kQ8Tile),       // PH_Q8S
     };
     sym_cnt[i] = cnt[PH_SYM];
     prod_cnt[i] = cnt[PH_PROD];
@@ -172,7 +178,7 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
     pl.mat_off[i] = off;
     const size_t xb = align_up(static_cast<size_t>(d.s_pad) * d.l_pad * pl.esize, kAlign);
     const size_t sb = align_up(static_cast<size_t>(d.s_pad) * d.s_pad * pl.esize, kAlign);
-    off += 2 * xb + 2 * sb;
+    off += 2 * xb + 2 * sb + (fp8 ? 2 * f8_buffer_bytes(d.s_pad, d.l_pad) : 0);
   }
   pl.total_bytes = batch == 0 ? 0 : off;
   return MUON_OK;
@@ -188,7 +194,7 @@ void bind(Plan& pl, char* ws) {
     d.x[0] = base;
     d.x[1] = base + xb;
     d.gram = base + 2 * xb;
-    d.poly = base + 2 * xb + sb;
+    d.poly = base + 2 * xb + sb;  // the e4m3 buffers, if any, follow (f8_buffer)
   }
 }
 
@@ -387,11 +393,22 @@ int32_t drain_timing() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int32_t check_ns_params(const muon_ns_params* p) {
+int32_t check_ns_params(const muon_ns_params* p, int32_t dtype) {
   if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "params pointer is null");
   if (p->steps < 0) return fail(MUON_ERR_INVALID_ARG, "steps = %d is negative", p->steps);
   if (p->cu_budget < 0)
     return fail(MUON_ERR_INVALID_ARG, "cu_budget = %d is negative", p->cu_budget);
+  if (p->fp8_steps < 0)
+    return fail(MUON_ERR_INVALID_ARG, "fp8_steps = %d is negative", p->fp8_steps);
+  if (p->fp8_steps > 0) {
+    if (dtype != MUON_BF16)
+      return fail(MUON_ERR_INVALID_ARG, "fp8_steps needs bf16 tensors");
+    if (p->fp8_steps >= p->steps)
+      return fail(MUON_ERR_INVALID_ARG, "fp8_steps = %d: the last of the %d steps is bf16",
+                  p->fp8_steps, p->steps);
+    if (p->cu_budget != 0)
+      return fail(MUON_ERR_INVALID_ARG, "fp8_steps and cu_budget cannot be combined");
+  }
   if (!std::isfinite(p->a) || !std::isfinite(p->b) || !std::isfinite(p->c) ||
       !std::isfinite(p->eps) || p->eps < 0.f)
     return fail(MUON_ERR_INVALID_ARG, "Newton-Schulz coefficients must be finite and eps >= 0");
@@ -435,6 +452,48 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   const bool fused = pl.bf16 && ns.steps > 0;
   int32_t cur = 0;
   for (int k = 0; k < ns.steps; ++k) {
+    if (k < ns.fp8_steps) {
+      // e4m3 step: block-scaled e4m3 copies of X (and X^T), A, then B feed the
+      // three products; every result is stored in bf16 as in a bf16 step
+      {
+        TimedLaunch t(MUON_K_QUANT8, stream, timed);
+        if ((e = launch_quant8(c, pl.totals[PH_Q8X], Q8_X, cur)) != hipSuccess)
+          return hip_fail(e, "launch e4m3 copies of X");
+        t.done();
+      }
+      {
+        TimedLaunch t(MUON_K_GRAM8, stream, timed);
+        if ((e = launch_gram8(c, pl.split_gram, use_poly ? 1.f : ns.b, k == 0)) != hipSuccess)
+          return hip_fail(e, "launch Gram (e4m3)");
+        t.done();
+      }
+      {
+        TimedLaunch t(MUON_K_QUANT8, stream, timed);
+        if ((e = launch_quant8(c, pl.totals[PH_Q8S], Q8_A, cur)) != hipSuccess)
+          return hip_fail(e, "launch e4m3 copy of A");
+        t.done();
+      }
+      if (use_poly) {
+        {
+          TimedLaunch t(MUON_K_POLY8, stream, timed);
+          if ((e = launch_poly8(c, pl.split_poly, ns.b, ns.c)) != hipSuccess)
+            return hip_fail(e, "launch polynomial (e4m3)");
+          t.done();
+        }
+        TimedLaunch t(MUON_K_QUANT8, stream, timed);
+        if ((e = launch_quant8(c, pl.totals[PH_Q8S], Q8_B, cur)) != hipSuccess)
+          return hip_fail(e, "launch e4m3 copy of B");
+        t.done();
+      }
+      {
+        TimedLaunch t(MUON_K_PROD8, stream, timed);
+        if ((e = launch_prod8(c, pl.split_prod, cur, ns.a, k == 0)) != hipSuccess)
+          return hip_fail(e, "launch product (e4m3)");
+        t.done();
+      }
+      cur ^= 1;
+      continue;
+    }
     {
       TimedLaunch t(MUON_K_GRAM, stream, timed);
       if ((e = launch_gram(c, pl.split_gram, pl.bf16, cur, use_poly ? 1.f : ns.b, k == 0)) !=
@@ -491,6 +550,12 @@ extern "C" size_t muon_workspace_bytes(int32_t batch, const int64_t* rows, const
   return pl.total_bytes;
 }
 
+extern "C" size_t muon_workspace_bytes_fp8(int32_t batch, const int64_t* rows, const int64_t* cols) {
+  Plan pl;
+  if (make_plan(batch, rows, cols, MUON_BF16, pl, /*fp8=*/true) != MUON_OK) return SIZE_MAX;
+  return pl.total_bytes;
+}
+
 namespace muon {
 namespace {
 
@@ -537,9 +602,9 @@ extern "C" int32_t muon_ns_batched(int32_t batch, const int64_t* rows, const int
   try {
     g_detail.clear();
     Plan pl;
-    int32_t st = make_plan(batch, rows, cols, dtype, pl);
+    int32_t st = make_plan(batch, rows, cols, dtype, pl, p != nullptr && p->fp8_steps > 0);
     if (st != MUON_OK) return st;
-    if ((st = check_ns_params(p)) != MUON_OK) return st;
+    if ((st = check_ns_params(p, dtype)) != MUON_OK) return st;
     if (batch == 0) return MUON_OK;
     if ((st = check_ns_pointers(batch, x, out)) != MUON_OK) return st;
     if ((st = check_ws(pl, workspace, workspace_bytes)) != MUON_OK) return st;
@@ -562,9 +627,9 @@ extern "C" int32_t muon_ns_batched_noalloc(int32_t batch, const int64_t* rows, c
   try {
     g_detail.clear();
     Plan pl;
-    int32_t st = make_plan(batch, rows, cols, dtype, pl);
+    int32_t st = make_plan(batch, rows, cols, dtype, pl, p != nullptr && p->fp8_steps > 0);
     if (st != MUON_OK) return st;
-    if ((st = check_ns_params(p)) != MUON_OK) return st;
+    if ((st = check_ns_params(p, dtype)) != MUON_OK) return st;
     if (batch == 0) return MUON_OK;
     if ((st = check_ns_pointers(batch, x, out)) != MUON_OK) return st;
     if (pl.total_bytes > MUON_NOALLOC_MAX_WORKSPACE)
@@ -593,10 +658,10 @@ extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const i
   try {
     g_detail.clear();
     Plan pl;
-    int32_t st = make_plan(batch, rows, cols, dtype, pl);
+    int32_t st = make_plan(batch, rows, cols, dtype, pl, p != nullptr && p->ns.fp8_steps > 0);
     if (st != MUON_OK) return st;
     if (p == nullptr) return fail(MUON_ERR_INVALID_ARG, "params pointer is null");
-    if ((st = check_ns_params(&p->ns)) != MUON_OK) return st;
+    if ((st = check_ns_params(&p->ns, dtype)) != MUON_OK) return st;
     if (!std::isfinite(p->lr) || !std::isfinite(p->beta))
       return fail(MUON_ERR_INVALID_ARG, "lr and beta must be finite");
     if (p->nesterov != 0 && p->nesterov != 1)

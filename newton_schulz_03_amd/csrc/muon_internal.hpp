@@ -5,6 +5,8 @@
 //   [inv]       float[batch]: 1 / (||U||_F + eps) per matrix
 //   [partials]  float[prepare blocks]: per-block sums of squares (Frobenius norm)
 //   per matrix  X ping, X pong: s_pad x l_pad;  A (Gram), B (polynomial): s_pad x s_pad
+//               and, for calls with e4m3 steps (fp8_steps > 0), two e4m3 buffers of
+//               s_pad * l_pad bytes plus one scale byte per 32 of them (F8 layout below)
 // X ping starts out holding U itself; the first Gram and product scale by the
 // norm factor.
 // Every matrix is held in its wide orientation (short side first): a matrix
@@ -13,6 +15,19 @@
 // (256); the padding holds zeros, which the iteration keeps at zero, so the
 // product kernels need no bounds checks.  X, A and B are stored in slabs of
 // 256 x 32 elements (see slab_off in device_common.hpp).
+//
+// F8 layout (e4m3 steps): an e4m3 copy of a matrix with `ncols` columns is held
+// in slabs of 256 rows x 64 columns (16 KiB, the same bytes as a bf16 slab),
+// each row's 64 values in two blocks of 32 with one power-of-two scale each
+// (E8M0: 2^(byte - 127)).  The scales of slab k are the 512 bytes at
+// scales + 512 k, where scales = data + s_pad * l_pad (the buffer's capacity);
+// the scale of row r (within the slab's 256) and block kb is byte
+// 4 * (32 * (2 * (r / 128) + kb) + r % 32) + (r / 32) % 4, so that one dword
+// holds the four scales a matrix-core lane needs per 64-wide K step.
+// Buffer 0 holds X (rows, blocks along the long side) for the Gram, then A,
+// then B (rows, blocks along the short side); buffer 1 holds X^T (rows of X^T,
+// blocks along X's short side) for the product.  Both follow B in the
+// workspace (f8_buffer).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,7 +46,14 @@ constexpr int kThreads = 256;       // threads per block, every kernel
 constexpr int kAlign = 256;         // workspace sub-buffer alignment
 constexpr int kXcd = 8;             // XCDs of the chip: workgroup b runs on XCD b % 8
 
-enum Phase : int { PH_PREPARE = 0, PH_SYM = 1, PH_PROD = 2, PH_FINISH = 3, PH_PRODW = 4, NPHASE = 5 };
+constexpr int kQ8Tile = 64;         // side of the e4m3 quantization tiles
+
+enum Phase : int {
+  PH_PREPARE = 0, PH_SYM = 1, PH_PROD = 2, PH_FINISH = 3, PH_PRODW = 4,
+  PH_Q8X = 5,  // e4m3 quantization of the iterate: kQ8Tile x kQ8Tile tiles of s_pad x l_pad
+  PH_Q8S = 6,  // e4m3 quantization of A or B: kQ8Tile x kQ8Tile tiles of s_pad x s_pad
+  NPHASE = 7
+};
 enum Mode : int { MODE_NS = 0, MODE_STEP = 1 };
 
 struct MatDesc {
@@ -40,7 +62,7 @@ struct MatDesc {
   void* dst;         // NS: out; STEP: w (updated in place)
   void* x[2];        // ping-pong iterate, s_pad x l_pad, wide orientation
   void* gram;        // A = X X^T, s_pad x s_pad
-  void* poly;        // B = b A + c A^2, s_pad x s_pad
+  void* poly;        // B = b A + c A^2, s_pad x s_pad; the e4m3 buffers follow it (f8_buffer)
   int64_t rows, cols, numel;  // user shape
   int32_t s, l;               // short and long side
   int32_t s_pad, l_pad;
@@ -77,6 +99,18 @@ struct ElemParams {
   int32_t cur;       // which X buffer holds the final iterate (finish)
   int32_t scale_x;   // finish: the iterate is still U (no iterations): scale by the norm factor
 };
+
+// Bytes of one e4m3 buffer of a matrix (s_pad * l_pad values and a scale byte
+// per 32), and the address of buffer k (0 or 1), which follow B (bf16, s_pad^2)
+// in the matrix's part of the workspace.
+__host__ __device__ __forceinline__ size_t f8_buffer_bytes(int64_t s_pad, int64_t l_pad) {
+  const size_t n = static_cast<size_t>(s_pad) * static_cast<size_t>(l_pad);
+  return (n + n / 32 + kAlign - 1) / kAlign * kAlign;
+}
+__host__ __device__ __forceinline__ char* f8_buffer(const MatDesc& d, int k) {
+  const size_t sb = (static_cast<size_t>(d.s_pad) * d.s_pad * 2 + kAlign - 1) / kAlign * kAlign;
+  return static_cast<char*>(d.poly) + sb + k * f8_buffer_bytes(d.s_pad, d.l_pad);
+}
 
 // AdamW over a ragged batch of flat tensors.
 struct AdamDesc {
@@ -132,6 +166,20 @@ hipError_t launch_prod(const LaunchCtx& c, const XcdSplit& sp, bool is_bf16, int
 // same MFMAs in the same order.
 hipError_t launch_prod_wide(const LaunchCtx& c, const XcdSplit& sp, int32_t cur, float a,
                             bool use_poly, bool first);
+
+// e4m3 steps.  launch_quant8: e4m3 copies with one power-of-two scale per 32
+// elements along each row: Q8_X quantizes the iterate X[cur] into buffer 0
+// (rows) and buffer 1 (rows of X^T); Q8_A / Q8_B quantize A / B into buffer 0.
+enum Quant8Src : int { Q8_X = 0, Q8_A = 1, Q8_B = 2 };
+hipError_t launch_quant8(const LaunchCtx& c, int32_t nblocks, int32_t src, int32_t cur);
+// The matrix-core products on e4m3 operands (gemm_f8.hip), 256 x 256 tiles:
+//   GRAM  A = out_scale * F0 F0^T                (F0: buffer 0; f^2 in the first step)
+//   POLY  B = c * F0 F0^T + b * A                (F0 holds A; b A in fp32)
+//   PROD  X[cur^1] = F1 F0^T + a X[cur]          (F0 holds B, or A when c = 0; F1 = X^T;
+//                                                 f in the first step)
+hipError_t launch_gram8(const LaunchCtx& c, const XcdSplit& sp, float out_scale, bool first);
+hipError_t launch_poly8(const LaunchCtx& c, const XcdSplit& sp, float b, float cc);
+hipError_t launch_prod8(const LaunchCtx& c, const XcdSplit& sp, int32_t cur, float a, bool first);
 
 // The allocation-free entry point (noalloc_scratch.hip).  noalloc_scratch:
 // the device address of the library's scratch array on the current device

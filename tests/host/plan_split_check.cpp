@@ -35,6 +35,12 @@ hipError_t launch_prod_wide(const LaunchCtx&, const XcdSplit&, int32_t, float, b
 }
 hipError_t launch_adamw(const AdamCtx&, int32_t, bool, const AdamParams&) { return hipSuccess; }
 hipError_t noalloc_scratch(char**) { return hipErrorInvalidSymbol; }
+hipError_t launch_quant8(const LaunchCtx&, int32_t, int32_t, int32_t) { return hipSuccess; }
+hipError_t launch_gram8(const LaunchCtx&, const XcdSplit&, float, bool) { return hipSuccess; }
+hipError_t launch_poly8(const LaunchCtx&, const XcdSplit&, float, float) { return hipSuccess; }
+hipError_t launch_prod8(const LaunchCtx&, const XcdSplit&, int32_t, float, bool) {
+  return hipSuccess;
+}
 hipError_t launch_put_bytes(const void*, size_t, void*, hipStream_t) { return hipSuccess; }
 int64_t adamw_blocks(int64_t n) { return n; }
 }  // namespace muon

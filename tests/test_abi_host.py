@@ -18,7 +18,7 @@ FAKE = 0x7f0000000000  # aligned, never dereferenced
 def header_functions():
     text = open(nsa.HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(muon_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +36,7 @@ def test_every_declared_function_is_exported(lib):
 def test_kernel_names_follow_the_header_enum():
     text = open(nsa.HEADER_PATH).read()
     ids = {m.group(1).lower(): int(m.group(2))
-           for m in re.finditer(r"MUON_K_([A-Z_]+)\s*=\s*(\d+)", text)}
+           for m in re.finditer(r"MUON_K_([A-Z0-9_]+)\s*=\s*(\d+)", text)}
     count = ids.pop("count")
     assert count == len(nsa.KERNELS)
     assert {name: k for k, name in enumerate(nsa.KERNELS)} == ids
@@ -56,7 +56,7 @@ def expected_workspace(shapes, esize):
 
     batch = len(shapes)
     desc = 112  # sizeof(MatDesc)
-    total = up(desc * batch, 256) + up(4 * 5 * (batch + 1), 256)  # 5 phase prefix arrays
+    total = up(desc * batch, 256) + up(4 * 7 * (batch + 1), 256)  # 7 phase prefix arrays
     total += up(4 * batch, 256)  # per-matrix 1 / (||U|| + eps)
     # one partial sum of squares per momentum-pass tile of the padded wide
     # iterate: 32 x 256 for a wide matrix (rows <= cols), 128 x 128 for a tall one
@@ -227,3 +227,31 @@ def test_ns_noalloc_validation(lib):
     st = lib.muon_ns_batched_noalloc(1, _i64_array([big]), _i64_array([big]), ptrs, ptrs, 0,
                                      ctypes.byref(p), None)
     assert st == nsa.MUON_ERR_WORKSPACE and "allocation-free" in nsa.last_error_detail()
+
+
+def test_fp8_steps_validation(lib):
+    """fp8_steps: bf16 only, fewer than steps, no CU budget; the workspace of such
+    a call is muon_workspace_bytes_fp8() (two e4m3 buffers per matrix more)."""
+    shapes = [(300, 700), (700, 300)]
+    rows, cols = _i64_array([r for r, _ in shapes]), _i64_array([c for _, c in shapes])
+    plain = nsa.workspace_bytes(shapes, nsa.MUON_BF16)
+    fp8 = nsa.workspace_bytes(shapes, nsa.MUON_BF16, fp8=True)
+    up = lambda x, a: -(-x // a) * a
+    extra = 0
+    for r, c in shapes:
+        n = up(min(r, c), 256) * up(max(r, c), 256)
+        extra += 2 * up(n + n // 32, 256)  # two e4m3 buffers: values, then a scale per 32
+    assert fp8 == plain + extra
+    ptrs = _ptr_array([FAKE, FAKE + (1 << 24)])
+    for dtype, steps, f8, budget, ws in [(nsa.MUON_FP32, 5, 2, 0, fp8), (nsa.MUON_BF16, 5, 5, 0, fp8),
+                                         (nsa.MUON_BF16, 5, -1, 0, fp8), (nsa.MUON_BF16, 5, 2, 8, fp8),
+                                         (nsa.MUON_BF16, 0, 1, 0, fp8)]:
+        p = NsParams(steps, 3.4445, -4.775, 2.0315, 1e-7, budget, f8)
+        st = lib.muon_ns_batched(2, rows, cols, ptrs, ptrs, dtype, ctypes.byref(p),
+                                 ctypes.c_void_p(FAKE), ws, None)
+        assert st == nsa.MUON_ERR_INVALID_ARG, (dtype, steps, f8, budget)
+    # a valid e4m3 call with the plain workspace size is refused as too small
+    p = NsParams(5, 3.4445, -4.775, 2.0315, 1e-7, 0, 2)
+    st = lib.muon_ns_batched(2, rows, cols, ptrs, ptrs, nsa.MUON_BF16, ctypes.byref(p),
+                             ctypes.c_void_p(FAKE), plain, None)
+    assert st == nsa.MUON_ERR_WORKSPACE
