@@ -264,6 +264,68 @@ def bench_hbm_ceiling(args) -> int:
     return 0
 
 
+def bench_link_ceiling(args) -> int:
+    """The host link with plain DMA copies between pinned host memory and HBM, in
+    the momentum's tensor sizes on the benchmark workload (96 bf16 tensors of
+    2048 x 6144): host to device, device to host, and both at once on two
+    streams; then the same two copies concurrent with an orthogonalization of
+    the 96 matrices.  The lower bound of a step with the momentum in host
+    memory is the time to move it both ways."""
+    import torch
+
+    import newton_schulz_03_amd as nsa
+
+    dev = torch.device("cuda:0")
+    n, per = 96, 2048 * 6144
+    host = [torch.empty(per, dtype=torch.bfloat16).pin_memory() for _ in range(n)]
+    back = [torch.empty(per, dtype=torch.bfloat16).pin_memory() for _ in range(n)]
+    devb = [torch.empty(per, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    devc = [torch.empty(per, dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    s_in, s_out = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    gb = n * per * 2 / 1e9
+
+    def h2d():
+        with torch.cuda.stream(s_in):
+            for h, d in zip(host, devb):
+                d.copy_(h, non_blocking=True)
+
+    def d2h():
+        with torch.cuda.stream(s_out):
+            for h, d in zip(back, devc):
+                h.copy_(d, non_blocking=True)
+
+    xs = [torch.randn(2048, 6144, device=dev).to(torch.bfloat16) for _ in range(n)]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = nsa.allocate_workspace([(2048, 6144)] * n, torch.bfloat16, dev)
+
+    def ns():
+        nsa.ns_batched(xs, steps=5, out=outs, workspace=ws)
+
+    def best_ms(fn):
+        times = []
+        for _ in range(max(2, args.steps)):
+            torch.cuda.synchronize(dev)
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize(dev)
+            times.append((time.perf_counter() - t0) * 1e3)
+        return sorted(times)[len(times) // 2]
+
+    res = {}
+    for name, fn, vol in (("h2d", h2d, gb), ("d2h", d2h, gb), ("both", lambda: (h2d(), d2h()), 2 * gb)):
+        fn()
+        ms = best_ms(fn)
+        res[name] = {"ms": round(ms, 2), "gbs": round(vol / ms * 1e3, 1)}
+        print(f"[bench] link {name}: {ms:.1f} ms", file=sys.stderr, flush=True)
+    ns()
+    res["ns_alone"] = {"ms": round(best_ms(ns), 2)}
+    res["ns_with_both_copies"] = {"ms": round(best_ms(lambda: (h2d(), d2h(), ns())), 2)}
+    print(json.dumps({"metric": "host link ceiling (pinned host memory <-> HBM, DMA copies)",
+                      "unit": "GB/s", "bytes_each_way": n * per * 2, "tensors": n,
+                      "median_of": max(2, args.steps), "patterns": res}), flush=True)
+    return 0
+
+
 def _cu_masked_stream(mask_words):
     """A HIP stream restricted to the CUs set in `mask_words` (32-bit words), at the
     default priority; returned as (torch ExternalStream, raw handle)."""
@@ -426,6 +488,8 @@ def main(argv=None) -> int:
     ap.add_argument("--hbm-bytes", type=int, default=96 * 2048 * 6144 * 2,
                     help="bytes per stream for --hbm-ceiling (default: one bf16 tensor of the "
                          "benchmark workload, 96 x 2048 x 6144)")
+    ap.add_argument("--link-ceiling", action="store_true",
+                    help="measure the host link with plain DMA copies of the momentum's size")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling hardware traffic counters)")
@@ -452,6 +516,8 @@ def main(argv=None) -> int:
         return bench_overlap(args)
     if args.hbm_ceiling:
         return bench_hbm_ceiling(args)
+    if args.link_ceiling:
+        return bench_link_ceiling(args)
     adamw = workloads.adamw_workloads()
     if args.workload in adamw:
         return bench_adamw(args, adamw[args.workload])
@@ -462,7 +528,8 @@ def main(argv=None) -> int:
     print(f"[bench] inputs resident in HBM after {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
     shapes = list(wl.shapes)
     tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    ws = nsa.allocate_workspace(shapes, tdt, dev, fp8=args.fp8_steps > 0)
+    ws = nsa.allocate_workspace(shapes, tdt, dev, fp8=args.fp8_steps > 0,
+                                momentum_host=args.momentum_host and wl.call == "step")
     c = wl.coeffs[2]
 
     if wl.call == "step":
@@ -528,13 +595,18 @@ def main(argv=None) -> int:
     alg_poly_launch = sum(min(s) ** 2 * (min(s) + 1) for s in shapes)
     peak = PEAK_TFLOPS[wl.dtype]
 
+    # with the momentum in host memory the step runs in chunks, one launch of
+    # each kernel per chunk, so a launch covers 1/nchunks of the batch's work
+    nchunks = max(1, round(kern["prepare"][1] / args.steps)) if args.momentum_host else 1
+
     def avg(name):
         ms, n = kern[name]
-        return ms / n if n else float("nan")
+        return ms * nchunks / n if n else float("nan")
 
     # the middle products (the first takes the norm factor, the last the update)
     prod_ms = avg("prod") if kern["prod"][1] else avg("prod_first")
     achieved = alg_prod_launch / (prod_ms * 1e-3) / 1e12
+    # avg_ms: per launch over the whole batch (the sum over a step's chunks)
     per_kernel = {k: {"avg_ms": round(avg(k), 4), "launches": kern[k][1]} for k in nsa.KERNELS
                   if kern[k][1]}
     ns_ms = sum(kern[k][0] for k in ("gram", "poly", "prod_first", "prod", "prod_finish", "quant8",
@@ -586,6 +658,8 @@ def main(argv=None) -> int:
         "per_kernel_pass_ms_per_step": round(instrumented_ms, 3),
         "kernels": per_kernel,
     }
+    if nchunks > 1:
+        result["momentum_chunks"] = nchunks
     if args.copy_calibration_mb > 0:
         # one plain copy of known size (reads n bytes, writes n bytes): hardware
         # traffic counters of the same run are scaled by what they read for it

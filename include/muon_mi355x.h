@@ -112,7 +112,7 @@ typedef struct {
    * fp8_steps = 2 of 5 the output is as close to the exact iteration as the
    * bf16 path's; more e4m3 steps are not (the polynomial amplifies their
    * noise once the singular values have grown).  Such a call needs
-   * muon_workspace_bytes_fp8() bytes of workspace. */
+   * muon_workspace_bytes_ex(..., MUON_WS_FP8) bytes of workspace. */
   int32_t fp8_steps;
 } muon_ns_params;
 
@@ -124,8 +124,19 @@ typedef struct {
  * when they move optimizer state off the accelerator ("Domyn is training a
  * 1T-parameter MoE on Europe's Jupiter supercomputer, and published the
  * recipe", §What moved the number, Offloading bullet).  Every m[i] must then be
- * pinned host memory (hipHostMalloc, or a pinned torch tensor); the step reads
- * M and writes the new momentum there in place, over the host link, once each.
+ * pinned host memory (hipHostMalloc, or a pinned torch tensor), updated in
+ * place.  The batch then runs in up to 16 chunks of about equal momentum bytes:
+ * a chunk's momentum is copied to the device by DMA, updated there, and copied
+ * back as soon as the momentum pass is done, on two library-owned streams of
+ * default priority, so that the copies of neighbouring chunks overlap this
+ * chunk's Newton-Schulz work.  The results are bit-identical to momentum in
+ * device memory.  The workspace must hold
+ * muon_workspace_bytes_ex(..., MUON_WS_MOMENTUM_HOST) bytes, and m[i] must not
+ * be touched by the host until the stream has finished the work.  Such a call
+ * may block the calling thread: it first waits until the previous such call on
+ * this device has finished on the GPU (with the copies of two calls queued at
+ * once, the copies slow down by a large and varying factor).  It cannot be
+ * captured into a HIP graph.
  * Otherwise (0) m[i] are device memory.
  */
 typedef struct {
@@ -145,12 +156,20 @@ typedef struct {
 size_t muon_workspace_bytes(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype);
 
 /*
- * Bytes of device workspace a bf16 call with fp8_steps > 0 needs over this
- * batch: muon_workspace_bytes() plus two e4m3 copies of each padded iterate
- * (s_pad * l_pad bytes each, plus a scale byte per 32).  Returns SIZE_MAX on
- * invalid arguments.  Host-only.
+ * Bytes of device workspace a call with the options in `flags` needs:
+ *   MUON_WS_FP8            a bf16 call with fp8_steps > 0: two e4m3 copies of
+ *                          each padded iterate more (s_pad * l_pad bytes each,
+ *                          plus a scale byte per 32)
+ *   MUON_WS_MOMENTUM_HOST  a step with momentum_host = 1: the batch runs in up
+ *                          to 16 chunks, each with its own part, plus two
+ *                          staging slots for a chunk's momentum
+ * flags = 0 is muon_workspace_bytes().  Returns SIZE_MAX on invalid arguments
+ * or unknown flags.  Host-only.
  */
-size_t muon_workspace_bytes_fp8(int32_t batch, const int64_t* rows, const int64_t* cols);
+#define MUON_WS_FP8 1u
+#define MUON_WS_MOMENTUM_HOST 2u
+size_t muon_workspace_bytes_ex(int32_t batch, const int64_t* rows, const int64_t* cols,
+                               int32_t dtype, uint32_t flags);
 
 /*
  * Orthogonalize a ragged batch: out[i] = NS_k(x[i]) (shape rows[i] x cols[i]).

@@ -23,7 +23,7 @@ SIZE_MAX = ctypes.c_size_t(-1).value
 QUINTIC = (3.4445, -4.7750, 2.0315)
 CUBIC = (1.5, -0.5, 0.0)
 
-EXPORTED = ("muon_workspace_bytes", "muon_workspace_bytes_fp8", "muon_ns_batched",
+EXPORTED = ("muon_workspace_bytes", "muon_workspace_bytes_ex", "muon_ns_batched",
             "muon_ns_batched_noalloc",
             "muon_step_batched",
             "muon_adamw_workspace_bytes", "muon_adamw_batched",
@@ -75,8 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_size_t)
     lib.muon_workspace_bytes.argtypes = [i32, i64p, i64p, i32]
     lib.muon_workspace_bytes.restype = sz
-    lib.muon_workspace_bytes_fp8.argtypes = [i32, i64p, i64p]
-    lib.muon_workspace_bytes_fp8.restype = sz
+    lib.muon_workspace_bytes_ex.argtypes = [i32, i64p, i64p, i32, ctypes.c_uint32]
+    lib.muon_workspace_bytes_ex.restype = sz
     lib.muon_ns_batched.argtypes = [i32, i64p, i64p, vpp, vpp, i32, ctypes.POINTER(NsParams), vp,
                                     sz, vp]
     lib.muon_ns_batched.restype = i32
@@ -139,15 +139,20 @@ def _dtype_code(dtype) -> int:
     raise TypeError(f"unsupported dtype {dtype}: use torch.bfloat16 or torch.float32")
 
 
-def workspace_bytes(shapes: Sequence[Tuple[int, int]], dtype, fp8: bool = False) -> int:
+MUON_WS_FP8, MUON_WS_MOMENTUM_HOST = 1, 2
+
+
+def workspace_bytes(shapes: Sequence[Tuple[int, int]], dtype, fp8: bool = False,
+                    momentum_host: bool = False) -> int:
     """Device workspace bytes for a batch of (rows, cols) shapes (fp8: for a bf16
-    call with e4m3 steps)."""
+    call with e4m3 steps; momentum_host: for a step with the momentum in host memory)."""
     lib = load_library()
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     rows = _i64_array([int(r) for r, _ in shapes])
     cols = _i64_array([int(c) for _, c in shapes])
-    if fp8:
-        n = lib.muon_workspace_bytes_fp8(len(shapes), rows, cols)
+    flags = (MUON_WS_FP8 if fp8 else 0) | (MUON_WS_MOMENTUM_HOST if momentum_host else 0)
+    if flags:
+        n = lib.muon_workspace_bytes_ex(len(shapes), rows, cols, code, flags)
     else:
         n = lib.muon_workspace_bytes(len(shapes), rows, cols, code)
     if n == SIZE_MAX:
@@ -155,12 +160,12 @@ def workspace_bytes(shapes: Sequence[Tuple[int, int]], dtype, fp8: bool = False)
     return int(n)
 
 
-def allocate_workspace(shapes, dtype, device, fp8: bool = False):
+def allocate_workspace(shapes, dtype, device, fp8: bool = False, momentum_host: bool = False):
     """A uint8 device tensor usable as the workspace of a call over `shapes`
-    (fp8: with e4m3 steps)."""
+    (fp8: with e4m3 steps; momentum_host: a step with the momentum in host memory)."""
     import torch
 
-    n = workspace_bytes(shapes, dtype, fp8)
+    n = workspace_bytes(shapes, dtype, fp8, momentum_host)
     ws = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + max(n, 1)]
@@ -265,8 +270,9 @@ def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, bet
                  fp8_steps: int = 0) -> None:
     """One Muon step over a ragged batch, in place on ws (weights) and ms (momentum).
 
-    momentum_host: the momenta are pinned host tensors (pin_memory), which the
-    GPU reads and writes in place over the host link.
+    momentum_host: the momenta are pinned host tensors (pin_memory), updated in
+    place: the step copies them to the device and back in chunks, overlapped
+    with the Newton-Schulz work.
     """
     import torch
 
@@ -290,7 +296,8 @@ def step_batched(ws: Sequence, gs: Sequence, ms: Sequence, lr: float = 0.02, bet
         raise ValueError("w, g and m of one matrix must share a shape")
     code = _dtype_code(ws[0].dtype)
     if workspace is None:
-        workspace = allocate_workspace(shapes, ws[0].dtype, dev, fp8=fp8_steps > 0)
+        workspace = allocate_workspace(shapes, ws[0].dtype, dev, fp8=fp8_steps > 0,
+                                       momentum_host=momentum_host)
     a, b, c = (float(v) for v in coeffs)
     p = StepParams(float(lr), float(beta), 1 if nesterov else 0,
                    NsParams(int(steps), a, b, c, float(eps), int(cu_budget), int(fp8_steps)),

@@ -300,6 +300,19 @@ int32_t upload_table(const Plan& pl, void* ws, hipStream_t stream) {
       ws, stream);
 }
 
+// The descriptor table as kernel arguments (no staging buffer, nothing but
+// kernel launches on the stream): the allocation-free entry point, and the
+// chunks of a step with the momentum in host memory, whose small copies would
+// otherwise queue with the chunks' momentum copies.
+int32_t put_table(const Plan& pl, char* ws, hipStream_t stream) {
+  const size_t desc_bytes = sizeof(MatDesc) * pl.batch;
+  hipError_t e = launch_put_bytes(pl.desc.data(), desc_bytes, ws, stream);
+  if (e == hipSuccess)
+    e = launch_put_bytes(pl.prefix.data(), sizeof(int32_t) * pl.prefix.size(),
+                         ws + align_up(desc_bytes, kAlign), stream);
+  return e == hipSuccess ? MUON_OK : hip_fail(e, "launch descriptor copy");
+}
+
 // AdamW: descriptors, then the block prefix array.
 struct AdamPlan {
   int32_t batch = 0;
@@ -425,8 +438,10 @@ int32_t check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
 }
 
 // Enqueue the whole step after the table is in place.
+// after_prepare (optional): recorded on the stream once the prepare kernel,
+// the last reader and writer of the momentum, is enqueued.
 int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
-            const muon_ns_params& ns, bool timed = true) {
+            const muon_ns_params& ns, bool timed = true, hipEvent_t after_prepare = nullptr) {
   LaunchCtx c;
   c.desc = reinterpret_cast<const MatDesc*>(ws);
   c.prefix = reinterpret_cast<const int32_t*>(ws + align_up(sizeof(MatDesc) * pl.batch, kAlign));
@@ -442,6 +457,8 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
       return hip_fail(e, "launch momentum/iterate/sum-of-squares");
     t.done();
   }
+  if (after_prepare != nullptr && (e = hipEventRecord(after_prepare, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord (after the momentum pass)");
   {
     TimedLaunch t(MUON_K_NORM, stream, timed);
     if ((e = launch_finalize(c, ep)) != hipSuccess) return hip_fail(e, "launch norm finalize");
@@ -538,6 +555,177 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   return MUON_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Momentum in pinned host memory.  The batch goes in up to kMaxChunks
+// contiguous chunks of about equal momentum bytes, each a call of its own (its
+// plan, table and part of the workspace).  Chunk k's momentum is copied to the
+// device by DMA on an internal copy-in stream, into one of two staging slots
+// that follow the chunks' parts of the workspace; the prepare kernel updates it
+// there in place, and an internal copy-out stream copies it back as soon as
+// that kernel is done.  So the host-link traffic of chunks k - 1 and k + 1
+// overlaps chunk k's Newton-Schulz work.  Events order the three streams; the
+// caller's stream waits for the last copy back, and the first copy in waits
+// for the work enqueued on the caller's stream before the call.  Each chunk's
+// matrices take the same kernels as in one call over the whole batch, so the
+// results are the same bits.
+constexpr int kMaxChunks = 16;
+
+struct ChunkPlan {
+  std::vector<int32_t> first;     // chunk k: matrices [first[k], first[k + 1])
+  std::vector<Plan> plans;
+  std::vector<size_t> ws_off;     // workspace offset of chunk k's part
+  std::vector<size_t> stage_off;  // per matrix: offset of its momentum within its chunk's slot
+  std::vector<size_t> bytes;      // per matrix: momentum bytes
+  size_t staging_off = 0;         // the two slots, staging_bytes each
+  size_t staging_bytes = 0;
+  size_t total_bytes = 0;
+};
+
+// The shapes must have passed make_plan.
+int32_t make_chunks(int32_t batch, const int64_t* rows, const int64_t* cols, int32_t dtype,
+                    bool fp8, ChunkPlan& cp) {
+  const size_t esize = dtype == MUON_BF16 ? 2 : 4;
+  cp.stage_off.assign(batch, 0);
+  cp.bytes.assign(batch, 0);
+  size_t total = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    cp.bytes[i] = esize * static_cast<size_t>(rows[i]) * static_cast<size_t>(cols[i]);
+    total += align_up(cp.bytes[i], kAlign);
+  }
+  const size_t target = (total + kMaxChunks - 1) / kMaxChunks;  // so at most kMaxChunks chunks
+  cp.first.assign(1, 0);
+  size_t acc = 0;
+  for (int32_t i = 0; i < batch; ++i) {
+    cp.stage_off[i] = acc;
+    acc += align_up(cp.bytes[i], kAlign);
+    if (acc >= target || i + 1 == batch) {
+      cp.staging_bytes = std::max(cp.staging_bytes, acc);
+      cp.first.push_back(i + 1);
+      acc = 0;
+    }
+  }
+  const int nchunks = static_cast<int>(cp.first.size()) - 1;
+  cp.plans.assign(nchunks, Plan{});
+  cp.ws_off.assign(nchunks, 0);
+  size_t off = 0;
+  for (int k = 0; k < nchunks; ++k) {
+    const int32_t a = cp.first[k];
+    const int32_t st = make_plan(cp.first[k + 1] - a, rows + a, cols + a, dtype, cp.plans[k], fp8);
+    if (st != MUON_OK) return st;
+    cp.ws_off[k] = off;
+    off += align_up(cp.plans[k].total_bytes, kAlign);
+  }
+  cp.staging_off = off;
+  cp.total_bytes = off + 2 * cp.staging_bytes;
+  return MUON_OK;
+}
+
+// The internal streams (default priority) and events of the chunked calls on
+// one device, created on first use and kept until the process ends.
+struct CopyStreams {
+  hipStream_t in = nullptr, out = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t in_done[kMaxChunks], prep_done[kMaxChunks], out_done[kMaxChunks];
+  hipEvent_t done = nullptr;  // the end of the last call
+  bool pending = false;       // done has been recorded
+  std::mutex mu;  // one chunked call enqueues at a time on a device
+};
+std::mutex g_copy_mu;
+std::map<int, CopyStreams*> g_copy;
+
+int32_t copy_streams(CopyStreams** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_copy_mu);
+  auto it = g_copy.find(dev);
+  if (it != g_copy.end()) {
+    *out = it->second;
+    return MUON_OK;
+  }
+  CopyStreams* cs = new CopyStreams();
+  if ((e = hipStreamCreateWithFlags(&cs->in, hipStreamNonBlocking)) != hipSuccess ||
+      (e = hipStreamCreateWithFlags(&cs->out, hipStreamNonBlocking)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&cs->start, hipEventDisableTiming)) != hipSuccess)
+    return hip_fail(e, "creating the copy streams");
+  if ((e = hipEventCreateWithFlags(&cs->done, hipEventDisableTiming | hipEventBlockingSync)) !=
+      hipSuccess)
+    return hip_fail(e, "creating the copy events");
+  for (int k = 0; k < kMaxChunks; ++k) {
+    if ((e = hipEventCreateWithFlags(&cs->in_done[k], hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&cs->prep_done[k], hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&cs->out_done[k], hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "creating the copy events");
+  }
+  g_copy[dev] = cs;
+  *out = cs;
+  return MUON_OK;
+}
+
+// Enqueues the chunked step (see above).  m[i] are pinned host pointers.
+int32_t run_chunked(ChunkPlan& cp, char* ws, hipStream_t user, const ElemParams& ep,
+                    const muon_ns_params& ns, void* const* w, const void* const* g,
+                    void* const* m) {
+  CopyStreams* cs = nullptr;
+  int32_t st = copy_streams(&cs);
+  if (st != MUON_OK) return st;
+  std::lock_guard<std::mutex> lock(cs->mu);
+  hipError_t e;
+  auto ok = [&](hipError_t r, const char* what) -> bool {
+    e = r;
+    if (r == hipSuccess) return true;
+    st = hip_fail(r, what);
+    return false;
+  };
+  // The previous call on this device must have finished before this one is
+  // enqueued.  With the copies of two calls queued at once, the runtime has
+  // been measured to move part of them onto shader copies that queue behind
+  // the Newton-Schulz kernels, and calls then took two to four times as long.
+  if (cs->pending && !ok(hipEventSynchronize(cs->done), "hipEventSynchronize")) return st;
+  if (!ok(hipEventRecord(cs->start, user), "hipEventRecord") ||
+      !ok(hipStreamWaitEvent(cs->in, cs->start, 0), "hipStreamWaitEvent") ||
+      !ok(hipStreamWaitEvent(cs->out, cs->start, 0), "hipStreamWaitEvent"))
+    return st;
+  const int nchunks = static_cast<int>(cp.plans.size());
+  for (int k = 0; k < nchunks; ++k) {
+    const int32_t a = cp.first[k], b = cp.first[k + 1];
+    char* slot = ws + cp.staging_off + static_cast<size_t>(k & 1) * cp.staging_bytes;
+    // copy in, once the slot's previous chunk has gone back to the host
+    if (k >= 2 && !ok(hipStreamWaitEvent(cs->in, cs->out_done[k - 2], 0), "hipStreamWaitEvent"))
+      return st;
+    for (int32_t i = a; i < b; ++i)
+      if (!ok(hipMemcpyAsync(slot + cp.stage_off[i], m[i], cp.bytes[i], hipMemcpyHostToDevice,
+                             cs->in), "hipMemcpyAsync (momentum to the device)"))
+        return st;
+    if (!ok(hipEventRecord(cs->in_done[k], cs->in), "hipEventRecord")) return st;
+    // the chunk's step, on the caller's stream
+    Plan& pl = cp.plans[k];
+    char* wsk = ws + cp.ws_off[k];
+    bind(pl, wsk);
+    for (int32_t i = a; i < b; ++i) {
+      MatDesc& d = pl.desc[i - a];
+      d.src = g[i];
+      d.dst = w[i];
+      d.mom = slot + cp.stage_off[i];
+    }
+    if (!ok(hipStreamWaitEvent(user, cs->in_done[k], 0), "hipStreamWaitEvent")) return st;
+    if ((st = put_table(pl, wsk, user)) != MUON_OK) return st;
+    if ((st = run(pl, wsk, user, ep, ns, true, cs->prep_done[k])) != MUON_OK) return st;
+    // copy back, as soon as the momentum pass is done
+    if (!ok(hipStreamWaitEvent(cs->out, cs->prep_done[k], 0), "hipStreamWaitEvent")) return st;
+    for (int32_t i = a; i < b; ++i)
+      if (!ok(hipMemcpyAsync(m[i], slot + cp.stage_off[i], cp.bytes[i], hipMemcpyDeviceToHost,
+                             cs->out), "hipMemcpyAsync (momentum to the host)"))
+        return st;
+    if (!ok(hipEventRecord(cs->out_done[k], cs->out), "hipEventRecord")) return st;
+  }
+  if (!ok(hipStreamWaitEvent(user, cs->out_done[nchunks - 1], 0), "hipStreamWaitEvent") ||
+      !ok(hipEventRecord(cs->done, user), "hipEventRecord"))
+    return st;
+  cs->pending = true;
+  return MUON_OK;
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -550,10 +738,24 @@ extern "C" size_t muon_workspace_bytes(int32_t batch, const int64_t* rows, const
   return pl.total_bytes;
 }
 
-extern "C" size_t muon_workspace_bytes_fp8(int32_t batch, const int64_t* rows, const int64_t* cols) {
+extern "C" size_t muon_workspace_bytes_ex(int32_t batch, const int64_t* rows, const int64_t* cols,
+                                          int32_t dtype, uint32_t flags) {
+  g_detail.clear();
+  if ((flags & ~(MUON_WS_FP8 | MUON_WS_MOMENTUM_HOST)) != 0) {
+    fail(MUON_ERR_INVALID_ARG, "unknown workspace flags 0x%x", flags);
+    return SIZE_MAX;
+  }
+  const bool fp8 = (flags & MUON_WS_FP8) != 0;
+  if (fp8 && dtype != MUON_BF16) {
+    fail(MUON_ERR_INVALID_ARG, "e4m3 steps need bf16 tensors");
+    return SIZE_MAX;
+  }
   Plan pl;
-  if (make_plan(batch, rows, cols, MUON_BF16, pl, /*fp8=*/true) != MUON_OK) return SIZE_MAX;
-  return pl.total_bytes;
+  if (make_plan(batch, rows, cols, dtype, pl, fp8) != MUON_OK) return SIZE_MAX;
+  if ((flags & MUON_WS_MOMENTUM_HOST) == 0 || batch == 0) return pl.total_bytes;
+  ChunkPlan cp;
+  if (make_chunks(batch, rows, cols, dtype, fp8, cp) != MUON_OK) return SIZE_MAX;
+  return cp.total_bytes;
 }
 
 namespace muon {
@@ -578,18 +780,6 @@ void bind_ns(Plan& pl, char* ws, const void* const* x, void* const* out) {
     pl.desc[i].mom = nullptr;
     pl.desc[i].dst = out[i];
   }
-}
-
-// The allocation-free variant of the orthogonalize-only call takes its
-// workspace from the library's scratch array (noalloc_scratch.hip) and sends
-// the descriptor table as kernel arguments.
-int32_t put_table(const Plan& pl, char* ws, hipStream_t stream) {
-  const size_t desc_bytes = sizeof(MatDesc) * pl.batch;
-  hipError_t e = launch_put_bytes(pl.desc.data(), desc_bytes, ws, stream);
-  if (e == hipSuccess)
-    e = launch_put_bytes(pl.prefix.data(), sizeof(int32_t) * pl.prefix.size(),
-                         ws + align_up(desc_bytes, kAlign), stream);
-  return e == hipSuccess ? MUON_OK : hip_fail(e, "launch descriptor copy");
 }
 
 }  // namespace
@@ -679,37 +869,41 @@ extern "C" int32_t muon_step_batched(int32_t batch, const int64_t* rows, const i
       if (w[i] == g[i] || w[i] == m[i] || static_cast<const void*>(m[i]) == g[i])
         return fail(MUON_ERR_INVALID_ARG, "matrix %d: w, g and m must be distinct buffers", i);
     }
-    if ((st = check_ws(pl, workspace, workspace_bytes)) != MUON_OK) return st;
-    char* ws = static_cast<char*>(workspace);
-    bind(pl, ws);
-    for (int32_t i = 0; i < batch; ++i) {
-      pl.desc[i].src = g[i];
-      pl.desc[i].dst = w[i];
-      if (p->momentum_host) {
-        // pinned host memory: the prepare kernel reads M and writes M' through
-        // its device mapping, once each; U goes to the iterate in HBM
-        hipPointerAttribute_t attr{};
-        hipError_t e = hipPointerGetAttributes(&attr, m[i]);
-        if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
-          (void)hipGetLastError();
-          return fail(MUON_ERR_INVALID_ARG,
-                      "matrix %d: momentum_host is set but m is not pinned host memory", i);
-        }
-        if (!aligned16(attr.devicePointer))
-          return fail(MUON_ERR_INVALID_ARG, "matrix %d: device mapping of m not 16-byte aligned", i);
-        pl.desc[i].mom = attr.devicePointer;
-      } else {
-        pl.desc[i].mom = m[i];
-      }
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if ((st = upload_table(pl, ws, s)) != MUON_OK) return st;
     ElemParams ep{};
     ep.mode = MODE_STEP;
     ep.nesterov = p->nesterov;
     ep.beta = p->beta;
     ep.eps = p->ns.eps;
     ep.lr = p->lr;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p->momentum_host) {
+      ChunkPlan cp;
+      if ((st = make_chunks(batch, rows, cols, dtype, p->ns.fp8_steps > 0, cp)) != MUON_OK) return st;
+      if (ws == nullptr || workspace_bytes < cp.total_bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes at %p; %zu bytes needed with the "
+                    "momentum in host memory", workspace_bytes, workspace, cp.total_bytes);
+      if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(MUON_ERR_INVALID_ARG, "workspace pointer %p is not 256-byte aligned", ws);
+      for (int32_t i = 0; i < batch; ++i) {
+        hipPointerAttribute_t attr{};
+        const hipError_t e = hipPointerGetAttributes(&attr, m[i]);
+        if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+          (void)hipGetLastError();
+          return fail(MUON_ERR_INVALID_ARG,
+                      "matrix %d: momentum_host is set but m is not pinned host memory", i);
+        }
+      }
+      return run_chunked(cp, ws, s, ep, p->ns, w, g, m);
+    }
+    if ((st = check_ws(pl, workspace, workspace_bytes)) != MUON_OK) return st;
+    bind(pl, ws);
+    for (int32_t i = 0; i < batch; ++i) {
+      pl.desc[i].src = g[i];
+      pl.desc[i].dst = w[i];
+      pl.desc[i].mom = m[i];
+    }
+    if ((st = upload_table(pl, ws, s)) != MUON_OK) return st;
     return run(pl, ws, s, ep, p->ns);
   } catch (...) {
     return fail(MUON_ERR_HIP, "unexpected host exception");

@@ -255,3 +255,28 @@ def test_fp8_steps_validation(lib):
     st = lib.muon_ns_batched(2, rows, cols, ptrs, ptrs, nsa.MUON_BF16, ctypes.byref(p),
                              ctypes.c_void_p(FAKE), plain, None)
     assert st == nsa.MUON_ERR_WORKSPACE
+
+
+def test_workspace_bytes_ex(lib):
+    """flags = 0 is the plain size; momentum in host memory adds the chunks' own
+    tables and two staging slots of at least an eighth of the momentum bytes;
+    unknown flags, or e4m3 steps with fp32, are refused."""
+    shapes = [(2048, 6144)] * 20 + [(300, 700), (700, 300)]
+    rows, cols = _i64_array([r for r, _ in shapes]), _i64_array([c for _, c in shapes])
+    plain = nsa.workspace_bytes(shapes, nsa.MUON_BF16)
+    assert lib.muon_workspace_bytes_ex(len(shapes), rows, cols, nsa.MUON_BF16, 0) == plain
+    host = nsa.workspace_bytes(shapes, nsa.MUON_BF16, momentum_host=True)
+    mbytes = sum(2 * r * c for r, c in shapes)
+    assert plain + 2 * mbytes // 8 <= host <= plain + 2 * mbytes // 4 + 8 * 4096
+    both = nsa.workspace_bytes(shapes, nsa.MUON_BF16, fp8=True, momentum_host=True)
+    assert both - host == nsa.workspace_bytes(shapes, nsa.MUON_BF16, fp8=True) - plain
+    assert lib.muon_workspace_bytes_ex(len(shapes), rows, cols, nsa.MUON_BF16, 4) == ctypes.c_size_t(-1).value
+    assert lib.muon_workspace_bytes_ex(len(shapes), rows, cols, nsa.MUON_FP32, 1) == ctypes.c_size_t(-1).value
+    # a step with the momentum in host memory and the plain workspace is refused
+    ptrs = _ptr_array([FAKE + (k << 26) for k in range(len(shapes))])
+    gp = _ptr_array([FAKE + (1 << 40) + (k << 26) for k in range(len(shapes))])
+    mp = _ptr_array([FAKE + (2 << 40) + (k << 26) for k in range(len(shapes))])
+    p = StepParams(0.02, 0.95, 0, NsParams(5, 3.4445, -4.775, 2.0315, 1e-7), 1)
+    st = lib.muon_step_batched(len(shapes), rows, cols, ptrs, gp, mp, nsa.MUON_BF16,
+                               ctypes.byref(p), ctypes.c_void_p(FAKE), plain, None)
+    assert st == nsa.MUON_ERR_WORKSPACE and "host memory" in nsa.last_error_detail()

@@ -435,13 +435,37 @@ def test_step_momentum_in_host_memory(dtype, nesterov):
         assert torch.equal(w_dev[i], w_host[i]) and torch.equal(m_dev[i].cpu(), m_host[i]), i
 
 
+@pytest.mark.parametrize("fp8_steps", [0, 2])
+def test_momentum_host_many_chunks(fp8_steps):
+    """Enough matrices for many chunks, so that both staging slots are reused
+    several times and the copies of neighbouring chunks overlap: bit-identical
+    to the momentum in HBM, over two steps (the second call waits for the
+    first)."""
+    rng = np.random.default_rng(17)
+    shapes = [tuple(int(v) for v in rng.choice([256, 513, 768, 1024], size=2)) for _ in range(26)]
+    wl = _wl("muon", "bf16", shapes)
+    ins = device_inputs(wl)
+    g = [d["g"] for d in ins]
+    w_dev = [d["w"].clone() for d in ins]
+    m_dev = [d["m"].clone() for d in ins]
+    w_host = [d["w"].clone() for d in ins]
+    m_host = [d["m"].cpu().pin_memory() for d in ins]
+    for _ in range(2):
+        nsa.step_batched(w_dev, g, m_dev, steps=5, fp8_steps=fp8_steps)
+        nsa.step_batched(w_host, g, m_host, steps=5, fp8_steps=fp8_steps, momentum_host=True)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        assert torch.equal(w_dev[i], w_host[i]), (i, shapes[i])
+        assert torch.equal(m_dev[i].cpu(), m_host[i]), (i, shapes[i])
+
+
 def test_momentum_host_rejects_device_memory():
     wl = _wl("muon", "bf16", [(64, 96)])
     d = device_inputs(wl)[0]
     lib = nsa.load_library()
     from newton_schulz_03_amd._binding import NsParams, StepParams, _i64_array, _ptr_array
     import ctypes
-    ws = nsa.allocate_workspace([(64, 96)], torch.bfloat16, "cuda")
+    ws = nsa.allocate_workspace([(64, 96)], torch.bfloat16, "cuda", momentum_host=True)
     p = StepParams(0.02, 0.95, 0, NsParams(5, 3.4445, -4.775, 2.0315, 1e-7), 1)
     st = lib.muon_step_batched(1, _i64_array([64]), _i64_array([96]), _ptr_array([d["w"].data_ptr()]),
                                _ptr_array([d["g"].data_ptr()]), _ptr_array([d["m"].data_ptr()]), 0,
