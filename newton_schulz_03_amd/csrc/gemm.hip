@@ -6,13 +6,12 @@
 //   PROD  X' = a X + alpha Q X   with Q = B (or A when c == 0)
 //
 // One 256x256 output tile per workgroup of 4 wavefronts (2x2, 128x128 each),
-// K staged through LDS 128 bytes at a time (64 bf16 or 32 fp32), double
-// buffered so that one barrier per K slice suffices.  Every operand is held in
-// LDS as rows of K ("K-major"), which is what a lane of the matrix core wants:
-// 8 consecutive bf16 of K per lane for v_mfma_f32_32x32x16_bf16 (4 fp32 feed
-// four v_mfma_f32_32x32x2_f32).  X, read as the right operand of Q X, is
-// K-major in memory only along its columns; its 8x8 (4x4) blocks are
-// transposed in registers on the way into LDS.  LDS rows are XOR-swizzled in
+// K staged through LDS 128 bytes (32 fp32) at a time, double buffered so that
+// one barrier per K slice suffices.  Every operand is held in LDS as rows of K
+// ("K-major"), which is what a lane of the matrix core wants: 4 consecutive
+// fp32 of K per lane feed four v_mfma_f32_32x32x2_f32.  X, read as the right
+// operand of Q X, is K-major in memory only along its columns; its 4x4 blocks
+// are transposed in registers on the way into LDS.  LDS rows are XOR-swizzled in
 // 16-byte chunks so that both the row-wise fills and the fragment reads spread
 // over the banks.
 #include "gemm_common.hpp"
@@ -57,15 +56,16 @@ struct KMajorTile {
   }
 };
 
-// A slab of BK rows (K) x 256 columns (N) of a row-major matrix, stored in LDS
-// transposed as 256 rows of K.  Moved in V x V blocks (V = elements per 16 B).
+// A slab of BK rows (K) x 256 columns (N) of a row-major fp32 matrix, stored in
+// LDS transposed as 256 rows of K.  Moved in 4 x 4 blocks (16 B per row).
 template <typename T>
 struct MNMajorTile {
+  static_assert(sizeof(T) == 4, "fp32 only: bf16 runs the kernels of gemm_bf16.hip");
   static constexpr int V = Elt<T>::kVec;
   static constexpr int BK = kRowBytes / sizeof(T);
   static constexpr int NB = kRowsPerOp / V;      // blocks along N
   static constexpr int KB = BK / V;              // blocks along K (8)
-  static constexpr int PER = NB * KB / kThreads;  // blocks per thread: 1 (bf16), 2 (fp32)
+  static constexpr int PER = NB * KB / kThreads;  // blocks per thread: 2
   u32x4_t r[PER][V];
   // rows [k0, k0 + BK) x columns [n0, n0 + 256) of a slab-layout matrix with ld columns
   __device__ __forceinline__ void load(const T* m, int64_t n0, int64_t ld, int64_t k0) {
@@ -85,34 +85,20 @@ struct MNMajorTile {
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         u32x4_t o;
-        if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int dw = 0; dw < 4; ++dw) {
-            const uint32_t lo = r[p][2 * dw][i >> 1], hi = r[p][2 * dw + 1][i >> 1];
-            o[dw] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-          }
-        } else {
-#pragma unroll
-          for (int dw = 0; dw < 4; ++dw) o[dw] = r[p][dw][i];
-        }
+        for (int dw = 0; dw < 4; ++dw) o[dw] = r[p][dw][i];
         lds_st16(lds, swz(nb * V + i, kb), o);
       }
     }
   }
 };
 
-// acc += P_frag * Q_frag over one 16-byte chunk of K per lane.
-template <typename T>
+// acc += P_frag * Q_frag over one 16-byte chunk of K (4 fp32) per lane.
 __device__ __forceinline__ void mfma_chunk(f32x16_t& acc, const u32x4_t& p, const u32x4_t& q) {
-  if constexpr (sizeof(T) == 2) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, p),
-                                                   __builtin_bit_cast(bf16x8_t, q), acc, 0, 0, 0);
-  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(p[e]), __uint_as_float(q[e]), acc,
-                                                 0, 0, 0);
-  }
+  for (int e = 0; e < 4; ++e)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(p[e]), __uint_as_float(q[e]), acc,
+                                               0, 0, 0);
 }
 
 }  // namespace
@@ -190,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) mfma_chunk<T>(acc[mi][ni], pf[mi], qf[ni]);
+        for (int ni = 0; ni < 4; ++ni) mfma_chunk(acc[mi][ni], pf[mi], qf[ni]);
     }
     if (more) {
       char* next = smem + ((kt + 1) & 1) * kStageBytes;

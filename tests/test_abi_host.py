@@ -259,7 +259,8 @@ def test_fp8_steps_validation(lib):
 
 def test_workspace_bytes_ex(lib):
     """flags = 0 is the plain size; momentum in host memory adds the chunks' own
-    tables and two staging slots of at least an eighth of the momentum bytes;
+    tables and two staging slots of a chunk each (at most 16 chunks: at least a
+    sixteenth of the momentum bytes, less than that plus one matrix);
     unknown flags, or e4m3 steps with fp32, are refused."""
     shapes = [(2048, 6144)] * 20 + [(300, 700), (700, 300)]
     rows, cols = _i64_array([r for r, _ in shapes]), _i64_array([c for _, c in shapes])
@@ -267,7 +268,8 @@ def test_workspace_bytes_ex(lib):
     assert lib.muon_workspace_bytes_ex(len(shapes), rows, cols, nsa.MUON_BF16, 0) == plain
     host = nsa.workspace_bytes(shapes, nsa.MUON_BF16, momentum_host=True)
     mbytes = sum(2 * r * c for r, c in shapes)
-    assert plain + 2 * mbytes // 8 <= host <= plain + 2 * mbytes // 4 + 8 * 4096
+    biggest = max(2 * r * c for r, c in shapes)
+    assert plain + 2 * mbytes // 16 <= host <= plain + 2 * (mbytes // 16 + biggest) + 16 * 4096
     both = nsa.workspace_bytes(shapes, nsa.MUON_BF16, fp8=True, momentum_host=True)
     assert both - host == nsa.workspace_bytes(shapes, nsa.MUON_BF16, fp8=True) - plain
     assert lib.muon_workspace_bytes_ex(len(shapes), rows, cols, nsa.MUON_BF16, 4) == ctypes.c_size_t(-1).value
