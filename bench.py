@@ -326,6 +326,79 @@ def bench_link_ceiling(args) -> int:
     return 0
 
 
+def bench_blas_compare(args) -> int:
+    """The vendor library's batched bf16 GEMM (torch.bmm, hipBLASLt) on the
+    products of one Newton-Schulz step of the benchmark workload, beside this
+    library's kernels on the same shapes: B X (2048x2048 @ 2048x6144), the full
+    X X^T (2048x6144 @ 6144x2048, which the library forms as upper tiles only)
+    and A A (2048^3), 96 of each, plus one 8192^3 product.  Medians of `steps`
+    timed batches of 10 launches."""
+    import torch
+
+    import newton_schulz_03_amd as nsa
+
+    dev = torch.device("cuda:0")
+    n, s, l = 96, 2048, 6144
+    peak = PEAK_TFLOPS["bf16"]
+    Bm = torch.randn(n, s, s, device=dev).to(torch.bfloat16)
+    X = torch.randn(n, s, l, device=dev).to(torch.bfloat16)
+    XT = X.transpose(1, 2).contiguous()
+    O = torch.empty(n, s, l, device=dev, dtype=torch.bfloat16)
+    A = torch.empty(n, s, s, device=dev, dtype=torch.bfloat16)
+    big = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    big_out = torch.empty_like(big)
+
+    def med_ms(fn):
+        fn()
+        torch.cuda.synchronize(dev)
+        times = []
+        for _ in range(max(3, args.steps)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(10):
+                fn()
+            b.record()
+            torch.cuda.synchronize(dev)
+            times.append(a.elapsed_time(b) / 10)
+        return sorted(times)[len(times) // 2]
+
+    res = {}
+    for name, fn, flops in (
+            ("prod B@X", lambda: torch.bmm(Bm, X, out=O), n * 2 * s * s * l),
+            ("gram X@X^T (full square)", lambda: torch.bmm(X, XT, out=A), n * 2 * s * s * l),
+            ("A@A (full square)", lambda: torch.bmm(Bm, Bm, out=A), n * 2 * s ** 3),
+            ("8192^3", lambda: torch.mm(big, big, out=big_out), 2 * 8192 ** 3)):
+        ms = med_ms(fn)
+        res[name] = {"ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
+                     "frac": round(flops / ms / 1e9 / peak, 4)}
+        print(f"[bench] torch {name}: {ms:.3f} ms", file=sys.stderr, flush=True)
+    del Bm, XT, O, A, big, big_out
+    xs = list(X.unbind(0))
+    outs = [torch.empty_like(x) for x in xs]
+    ws = nsa.allocate_workspace([(s, l)] * n, torch.bfloat16, dev)
+    nsa.ns_batched(xs, steps=5, out=outs, workspace=ws)
+    torch.cuda.synchronize(dev)
+    nsa.timing_reset()
+    nsa.timing_enable(True)
+    for _ in range(max(3, args.steps)):
+        nsa.ns_batched(xs, steps=5, out=outs, workspace=ws)
+    torch.cuda.synchronize(dev)
+    nsa.timing_enable(False)
+    kern = nsa.timing_read()
+    lib = {}
+    for name, key, flops in (("prod B@X", "prod", n * 2 * s * s * l),
+                             ("gram X@X^T (upper tiles)", "gram", n * s * (s + 1) * l),
+                             ("A@A (upper tiles)", "poly", n * s * s * (s + 1))):
+        ms = kern[key][0] / kern[key][1]
+        lib[name] = {"ms": round(ms, 3), "tflops": round(flops / ms / 1e9, 1),
+                     "frac": round(flops / ms / 1e9 / peak, 4)}
+    print(json.dumps({"metric": "bf16 GEMM: vendor library (torch.bmm) against this library's kernels",
+                      "unit": "TFLOP/s", "peak": peak, "batch": n, "note": "frac: algorithmic flops / "
+                      "bf16 dense peak; the library's symmetric products count s(s+1) per row pair",
+                      "torch": res, "library": lib}), flush=True)
+    return 0
+
+
 def _cu_masked_stream(mask_words):
     """A HIP stream restricted to the CUs set in `mask_words` (32-bit words), at the
     default priority; returned as (torch ExternalStream, raw handle)."""
@@ -488,6 +561,9 @@ def main(argv=None) -> int:
     ap.add_argument("--hbm-bytes", type=int, default=96 * 2048 * 6144 * 2,
                     help="bytes per stream for --hbm-ceiling (default: one bf16 tensor of the "
                          "benchmark workload, 96 x 2048 x 6144)")
+    ap.add_argument("--blas-compare", action="store_true",
+                    help="time the vendor library's batched GEMM on the step's products beside "
+                         "this library's kernels")
     ap.add_argument("--link-ceiling", action="store_true",
                     help="measure the host link with plain DMA copies of the momentum's size")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -518,6 +594,8 @@ def main(argv=None) -> int:
         return bench_hbm_ceiling(args)
     if args.link_ceiling:
         return bench_link_ceiling(args)
+    if args.blas_compare:
+        return bench_blas_compare(args)
     adamw = workloads.adamw_workloads()
     if args.workload in adamw:
         return bench_adamw(args, adamw[args.workload])
