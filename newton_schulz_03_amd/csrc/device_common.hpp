@@ -14,6 +14,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))  // LDS pointers, for the transposing reads
 
 // Storage types: bf16 is carried as its raw 16 bits.
 struct bf16_tag {};

@@ -86,8 +86,10 @@ struct UVec {
 // ---------------------------------------------------------------------------
 // k_prepare: one block per tile of the padded wide iterate: kPrepWideRows x
 // 256 for a wide matrix; kPrepTallS x kPrepTallL (short side x long side,
-// 128 x 128) for a tall one, which is read as the user's kPrepTallL x
-// kPrepTallS tile (rows of 256 bytes) and transposed through LDS.  Each
+// 256 x 64) for a tall one, which is read as the user's kPrepTallL x
+// kPrepTallS tile (bf16 rows of 512 bytes, as a wide tile's) and transposed
+// through LDS.  (Tiles of 128 x 128, rows of 256 bytes, ran the pass at 0.66
+// of the HBM peak against 0.72 for wide matrices.)  Each
 // thread moves 16-byte vectors v = it * 256 + threadIdx.x of the tile in
 // row-major order, so every load and store instruction of a wave covers whole
 // rows of the tile: contiguous runs of memory.  The transpose holds U already
@@ -121,6 +123,59 @@ __device__ __forceinline__ float prepare_vectors(const MatDesc& d, const ElemPar
   return acc;
 }
 
+// The bf16 tall tile (the user's kPrepTallL x kPrepTallS = 64 x 256, rows of
+// 512 bytes) into the wide iterate, transposed through LDS.  Each thread's 8
+// vectors go in as whole 16-byte row pieces (thread vector v: user row v / 32,
+// chunk v % 32).  They come out with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16): a 16-lane group reads 4 user rows x 16 user columns
+// (lanes 4r .. 4r + 3 take row r, 4 columns each) and lane j receives column j
+// of the 4 rows.  Two such reads give a lane 8 consecutive user rows of one
+// user column: one 16-byte vector of an iterate row.  Wave instruction I
+// (0..31) covers user columns 16 (I % 16) + 0..15 and user rows 32 (I / 16) +
+// 0..31: 16 iterate rows x 64 contiguous bytes of one slab.  Chunk k of user
+// row r sits at chunk k ^ (2 (r & 3) + 8 ((r >> 3) & 1)), so that the 4 rows x
+// 32 bytes of a group, and the two groups of a 32-lane half, fall on distinct
+// banks.
+__device__ __forceinline__ int tall_chunk(int row, int k) {
+  return k ^ (2 * (row & 3) + 8 * ((row >> 3) & 1));
+}
+
+__device__ __forceinline__ void transpose_tall_bf16(char* lds, const u32x4_t* up, uint16_t* xu,
+                                                    int64_t i0, int64_t j0, int64_t l_pad) {
+  constexpr int kRowB = kPrepTallS * 2;       // 512 bytes
+  constexpr int kChunks = kRowB / 16;         // 32 per user row
+  constexpr int kColBlocks = kPrepTallS / 16;  // 16 blocks of 16 user columns
+  constexpr int kNv = kPrepTallL * kPrepTallS / (8 * kThreads);  // vectors per thread
+  static_assert(kNv * 8 * kThreads == kPrepTallL * kPrepTallS && kPrepTallL % 32 == 0,
+                "whole vectors per thread; whole 32-row blocks");
+#pragma unroll
+  for (int it = 0; it < kNv; ++it) {
+    const int v = it * kThreads + threadIdx.x;
+    const int row = v / kChunks;
+    *reinterpret_cast<u32x4_t*>(lds + row * kRowB + (tall_chunk(row, v % kChunks) << 4)) = up[it];
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, rr = (lane >> 2) & 3, qq = lane & 3, j = lane & 15;
+#pragma unroll
+  for (int k = 0; k < kNv; ++k) {
+    const int I = kNv * wave + k;
+    const int wb = I % kColBlocks, cb = I / kColBlocks;
+    u32x4_t o;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * cb + 8 * g + 4 * h + rr;
+      const char* a = lds + row * kRowB + (tall_chunk(row, 2 * wb + (qq >> 1)) << 4) + 8 * (qq & 1);
+      const s16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4_t*)(a));
+      const u32x2_t xv = __builtin_bit_cast(u32x2_t, x);
+      o[2 * h] = xv[0];
+      o[2 * h + 1] = xv[1];
+    }
+    // iterate row i0 + 16 wb + j (a user column), columns j0 + 32 cb + 8 g .. + 7 (user rows)
+    st16_nt(xu + slab_off(i0 + 16 * wb + j, j0 + 32 * cb + 8 * g, l_pad), o);
+  }
+}
+
 }  // namespace
 
 template <typename T>
@@ -148,22 +203,33 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
     constexpr int vpr = kWideTileCols / V;
     u32x4_t up[kVecsWide];
     acc = prepare_vectors<T, kVecsWide>(d, p, i0, j0, vpr, up);
-    // V consecutive columns starting at a multiple of V stay inside one slab row
+    // V consecutive columns starting at a multiple of V stay inside one slab row.
+    // Nontemporal: U is far larger than the caches, and the first Gram reads it
+    // back from HBM (measured: the pass 1.5% faster than with cached stores).
 #pragma unroll
     for (int it = 0; it < kVecsWide; ++it) {
       const int v = it * kThreads + threadIdx.x;
-      st16(xu + slab_off(i0 + v / vpr, j0 + (v % vpr) * V, d.l_pad), up[it]);
+      st16_nt(xu + slab_off(i0 + v / vpr, j0 + (v % vpr) * V, d.l_pad), up[it]);
     }
   } else {
-    const int32_t tpr = d.l_pad / kTallRows;
-    const int64_t i0 = static_cast<int64_t>(t / tpr) * kTallCols;  // wide rows (short side)
-    const int64_t j0 = static_cast<int64_t>(t % tpr) * kTallRows;  // wide cols (long side)
+    // consecutive blocks take neighbouring column strips of the same user rows,
+    // so that together they read whole user rows (measured: in the other order,
+    // strips of one column across all rows, the pass ran 4% slower)
+    const int32_t tps = d.s_pad / kTallCols;
+    const int64_t i0 = static_cast<int64_t>(t % tps) * kTallCols;  // wide rows (short side)
+    const int64_t j0 = static_cast<int64_t>(t / tps) * kTallRows;  // wide cols (long side)
     constexpr int vpr = kTallCols / V;
     union Packed {
       u32x4_t v;
       T e[V];
     } up[kVecsTall];
     acc = prepare_vectors<T, kVecsTall>(d, p, j0, i0, vpr, &up[0].v);
+    if constexpr (sizeof(T) == 2) {
+      transpose_tall_bf16(reinterpret_cast<char*>(&tile[0][0]), &up[0].v, xu, i0, j0, d.l_pad);
+      const float total = block_sum(acc, scratch);
+      if (threadIdx.x == 0) c.partials[b] = total;
+      return;
+    }
 #pragma unroll
     for (int it = 0; it < kVecsTall; ++it) {
       const int v = it * kThreads + threadIdx.x;
@@ -182,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
       Packed o;
 #pragma unroll
       for (int e = 0; e < V; ++e) o.e[e] = tile[wcol + e][wrow];
-      st16(xu + slab_off(i0 + wrow, j0 + wcol, d.l_pad), o.v);
+      st16_nt(xu + slab_off(i0 + wrow, j0 + wcol, d.l_pad), o.v);
     }
   }
   const float total = block_sum(acc, scratch);

@@ -21,8 +21,6 @@ constexpr int LPO = OPB / (kThreads * 16);  // 16-byte loads per thread, operand
 constexpr int MNROW = kTile * 2;            // bytes of one MN-major LDS row (256 columns)
 static_assert(LDSB >= kTile * MNROW, "the tile store stages a whole 256 x 256 bf16 tile in the ring");
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
 
 // Chunk key of a K-major LDS row.  It depends on row bits 2 and 3 only: with a
 // key that varies with bit 1, gfx950 serves the fragment reads (ds_read_b128,

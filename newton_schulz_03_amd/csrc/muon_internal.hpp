@@ -38,8 +38,8 @@ namespace muon {
 constexpr int kTile = 256;          // GEMM output tile (both sides) and padding granularity
 constexpr int kTileW = 384;         // columns of X in a wide product tile (256 rows of B x 384)
 constexpr int kEwTile = 64;         // tile side of the finish kernel
-constexpr int kPrepTallS = 128;     // prepare's tall tiles: kPrepTallS (short side) x kPrepTallL
-constexpr int kPrepTallL = 128;     //   (long side) of the iterate, the user's kPrepTallL x kPrepTallS
+constexpr int kPrepTallS = 256;     // prepare's tall tiles: kPrepTallS (short side) x kPrepTallL
+constexpr int kPrepTallL = 64;      //   (long side) of the iterate, the user's kPrepTallL x kPrepTallS
 constexpr int kPrepWideRows = 32;   // prepare's wide tiles: kPrepWideRows x 256
 constexpr int kWideTileCols = 256;  // long-side width of prepare's wide tiles
 constexpr int kThreads = 256;       // threads per block, every kernel

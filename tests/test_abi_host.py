@@ -59,9 +59,9 @@ def expected_workspace(shapes, esize):
     total = up(desc * batch, 256) + up(4 * 7 * (batch + 1), 256)  # 7 phase prefix arrays
     total += up(4 * batch, 256)  # per-matrix 1 / (||U|| + eps)
     # one partial sum of squares per momentum-pass tile of the padded wide
-    # iterate: 32 x 256 for a wide matrix (rows <= cols), 128 x 128 for a tall one
+    # iterate: 32 x 256 for a wide matrix (rows <= cols), 256 x 64 for a tall one
     blocks = sum((up(r, 256) // 32) * (up(c, 256) // 256) if r <= c else
-                 (up(c, 256) // 128) * (up(r, 256) // 128) for r, c in shapes)
+                 (up(c, 256) // 256) * (up(r, 256) // 64) for r, c in shapes)
     total += up(4 * blocks, 256)
     for r, c in shapes:
         s, l = min(r, c), max(r, c)

@@ -98,7 +98,7 @@ def _workspace_f8(ws, shape, which):
     tall = r > c
     sp, lp = _up(min(shape), 256), _up(max(shape), 256)
     off = _up(112, 256) + _up(4 * 7 * 2, 256) + _up(4, 256)
-    blocks = (sp // 128) * (lp // 128) if tall else (sp // 32) * (lp // 256)
+    blocks = (sp // 256) * (lp // 64) if tall else (sp // 32) * (lp // 256)
     off += _up(4 * blocks, 256)
     off += 2 * _up(sp * lp * 2, 256) + 2 * _up(sp * sp * 2, 256)
     n = sp * lp
