@@ -145,6 +145,194 @@ __device__ __forceinline__ void store_final(const f32x16_t (&acc)[4][4], const T
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Diagonal tiles of the symmetric products (GRAM and POLY with ti == tj).  P
+// and Q are the same 256 rows, so only P is streamed into the ring (4 loads per
+// thread and slice, two in each half), and only the 36 blocks of 32 x 32 on or
+// above the block diagonal are formed, 9 per wave: wave W takes block rows W
+// and 7 - W, blocks (W, W..7) and (7 - W, 7 - W..7), from the fragments of
+// blocks W..7 alone (P and Q fragments are the same).  A full tile spends 64
+// MFMAs per wave and K step on 16 blocks; this spends 9 on 9.  Every block takes
+// the same MFMAs in the same order as in a full tile, the (b/c) A term of POLY
+// included, so the blocks on and above the diagonal are bit-identical to a full
+// tile's.  The blocks below are stored as the mirrors of those above, so the
+// stored A and B are exactly symmetric.
+template <int W>
+struct DiagWave {
+  static constexpr int kFrags = 8 - W;  // fragments of blocks W..7
+  static constexpr int kBlocks = 9;
+  static constexpr int row(int i) { return i < 8 - W ? W : 7 - W; }
+  static constexpr int col(int i) { return i < 8 - W ? W + i : 7 - W + (i - (8 - W)); }
+};
+
+template <int MODE, int W>
+__device__ __forceinline__ void diag_wave(const LaunchCtx& c, const GemmArgs& g, const TileRef& tr,
+                                          char* smem, int lane) {
+  using DW = DiagWave<W>;
+  constexpr int NF = DW::kFrags;
+  const int64_t s_pad = tr.d.s_pad, l_pad = tr.d.l_pad;
+  const uint16_t* src = MODE == GM_GRAM ? static_cast<const uint16_t*>(iterate(tr.d, g.cur))
+                                        : static_cast<const uint16_t*>(tr.d.gram);
+  const int64_t K = MODE == GM_GRAM ? l_pad : s_pad;
+  const Stream sp = kmajor_stream(src, tr.ti, K, W, lane);
+  const int nk = static_cast<int>(K / BK);
+  const int lr = lane & 31, lh = lane >> 5;
+  int32_t base[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) base[sub] = lr * KROW + (((2 * sub + lh) ^ kkey(lr)) << 4);
+
+  f32x16_t acc[DW::kBlocks];
+#pragma unroll
+  for (int i = 0; i < DW::kBlocks; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+
+  // the (b/c) A term (POLY): see gemm_tile
+  const __bf16 s_hi = static_cast<__bf16>(g.init_scale);
+  const __bf16 s_lo = static_cast<__bf16>(g.init_scale - static_cast<float>(s_hi));
+  auto ident = [&](int h, __bf16 v) {
+    bf16x8_t r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = lr == 16 * h + 8 * lh + e ? v : static_cast<__bf16>(0.f);
+    return r;
+  };
+  // term MFMAs of block row R (a compile-time row; -1: none), in column order
+  auto term_op = [&](const u32x4_t (&f)[NF], int h, auto R) {
+    constexpr int r = decltype(R)::value;
+    if constexpr (MODE == GM_POLY && r >= 0) {
+      const bf16x8_t id[2] = {ident(h, s_hi), ident(h, s_lo)};
+      static_for<DW::kBlocks>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        if constexpr (DW::row(i) == r) {
+#pragma unroll
+          for (int part = 0; part < 2; ++part)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                id[part], __builtin_bit_cast(bf16x8_t, f[DW::col(i) - W]), acc[i], 0, 0, 0);
+        }
+      });
+    }
+  };
+  auto mfma_op = [&](const u32x4_t (&f)[NF], auto I) {
+    constexpr int i = decltype(I)::value;
+    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8_t, f[DW::row(i) - W]), __builtin_bit_cast(bf16x8_t, f[DW::col(i) - W]),
+        acc[i], 0, 0, 0);
+  };
+
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)smem));
+  // prologue: slices 0..NST-2 (clamped as in gemm_tile), wait for slice 0
+#pragma unroll
+  for (int st = 0; st < NST - 1; ++st) sp.issue(st < nk ? st : nk - 1, ring + st * STAGEB);
+  wait_vm<(NST - 2) * LPO>();
+  __syncthreads();
+  u32x4_t f0[NF], f1[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) f0[f] = lds16(smem + base[0] + (W + f) * 32 * KROW);
+
+  auto slice = [&](int kt, auto R) {
+    const char* stage = smem + (kt & (NST - 1)) * STAGEB;
+    const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
+    const uint32_t fill = ring + ((kt + NST - 1) & (NST - 1)) * STAGEB;
+    const i32x4_t rp = sp.rsrc(ks);
+    term_op(f0, 0, R);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<DW::kBlocks>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i == 0 || i == 4) sp.issue_one(rp, fill, i / 4);
+      if constexpr (i < NF) f1[i] = lds16(stage + base[1] + (W + i) * 32 * KROW);
+      mfma_op(f0, I);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // slice kt+1 has landed once only slice kt+2 and half of kt+NST-1 remain
+    wait_vm<(NST - 3) * LPO + LPO / 2>();
+    wait_lgkm0();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    const char* next = smem + ((kt + 1) & (NST - 1)) * STAGEB;
+    term_op(f1, 1, R);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<DW::kBlocks>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i == 0 || i == 4) sp.issue_one(rp, fill, 2 + i / 4);
+      if constexpr (i < NF) f0[i] = lds16(next + base[0] + (W + i) * 32 * KROW);
+      mfma_op(f1, I);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  using NoTerm = std::integral_constant<int, -1>;
+  if constexpr (MODE == GM_GRAM) {
+    for (int kt = 0; kt < nk; ++kt) slice(kt, NoTerm{});
+  } else {
+    // the term slices of block rows W and 7 - W (both < nk)
+    const int r0 = 8 * tr.ti + W, r1 = 8 * tr.ti + 7 - W;
+    for (int kt = 0; kt < r0; ++kt) slice(kt, NoTerm{});
+    slice(r0, std::integral_constant<int, W>{});
+    for (int kt = r0 + 1; kt < r1; ++kt) slice(kt, NoTerm{});
+    slice(r1, std::integral_constant<int, 7 - W>{});
+    for (int kt = r1 + 1; kt < nk; ++kt) slice(kt, NoTerm{});
+  }
+  wait_vm<0>();  // no load may still target LDS: the ring is reused for the store
+  __syncthreads();
+
+  // T[q][p] = S[ti*256 + p][ti*256 + q] for the formed blocks (p's block <= q's),
+  // staged as in stage_tile
+  const float scale = g.out_scale * norm_factor<MODE>(c, g, tr);
+  static_for<DW::kBlocks>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const int q = 32 * DW::col(i) + lr;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const int ch = 4 * DW::row(i) + gg;
+      u32x2_t w;
+      w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 0])) |
+             (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 1])) << 16);
+      w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 2])) |
+             (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 3])) << 16);
+      *reinterpret_cast<u32x2_t*>(smem + q * MNROW + ((ch ^ (q & 31)) << 4) + 8 * lh) = w;
+    }
+  });
+}
+
+// The store of a diagonal tile: rows of T where p's block <= q's block go to
+// S[ti*256 + q][ti*256 + p] (on and below the diagonal), columns of T where
+// p's block < q's block to S[ti*256 + p][ti*256 + q] (above it).
+template <int MODE>
+__device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wave, int lane) {
+  uint16_t* dst = static_cast<uint16_t*>(MODE == GM_GRAM ? tr.d.gram : tr.d.poly);
+  const int64_t ld = tr.d.s_pad, o = static_cast<int64_t>(tr.ti) * kTile;
+  const int t = threadIdx.x, ch = t & 31;
+#pragma unroll 8
+  for (int u = 0; u < 32; ++u) {
+    const int q = (t >> 5) + 8 * u;
+    if ((ch >> 2) <= (q >> 5)) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((ch ^ (q & 31)) << 4));
+      st16(dst + slab_off(o + q, o + 8 * ch, ld), v);
+    }
+  }
+  const int grp = lane >> 4, j = lane & 15;
+#pragma unroll 4
+  for (int u = 0; u < 32; ++u) {
+    const int I = 32 * wave + u;
+    const int pb = I >> 3, cq = 4 * (I & 7) + grp;
+    if ((pb >> 1) < (cq >> 2))
+      st16(dst + slab_off(o + 16 * pb + j, o + 8 * cq, ld), read_tile_column(smem, I, lane));
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void diag_tile(const LaunchCtx& c, const GemmArgs& g, const TileRef& tr,
+                                          char* smem, int lane) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  switch (wave) {
+    case 0: diag_wave<MODE, 0>(c, g, tr, smem, lane); break;
+    case 1: diag_wave<MODE, 1>(c, g, tr, smem, lane); break;
+    case 2: diag_wave<MODE, 2>(c, g, tr, smem, lane); break;
+    default: diag_wave<MODE, 3>(c, g, tr, smem, lane); break;
+  }
+  __syncthreads();
+  diag_store<MODE>(tr, smem, wave, lane);
+}
+
 // One output tile (tile number t of the launch).  FINAL (products only): the last product
 // of a call, storing with store_final.  FIRST (products only): the first product of a
 // call, whose iterate is still U, scaled by the norm factor as it is stored.
@@ -162,6 +350,12 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   // the epilogue (which made the looping kernels spill more).
   int lane = threadIdx.x & 63;
   if constexpr (LOOP) asm volatile("" : "+v"(lane));
+  if constexpr (MODE != GM_PROD) {
+    if (tr.ti == tr.tj) {
+      diag_tile<MODE>(c, g, tr, smem, lane);
+      return;
+    }
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;

@@ -76,11 +76,6 @@ __device__ __forceinline__ void set_half(i32x8_t& f, int h, const u32x4_t& v) {
   for (int k = 0; k < 4; ++k) f[4 * h + k] = static_cast<int32_t>(v[k]);
 }
 
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for(F&& body, std::integer_sequence<int, Is...>) {
-  (body(std::integral_constant<int, Is>{}), ...);
-}
-
 // Adds the init_scale multiple of the source tile to the accumulators (lane
 // layout of gemm_common.hpp): PROD  a X[ti*256 + q][tj*256 + p];
 // POLY  (b/c) A[ti*256 + p][tj*256 + q], read as A[tj*256 + q][ti*256 + p] (A is

@@ -134,6 +134,17 @@ struct Frags {
   u32x4_t q[4];
 };
 
+// body(integral_constant<int, i>) for each i of the sequence, or of 0 .. N-1:
+// compile-time indices for register arrays and instruction operands.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for(F&& body, std::integer_sequence<int, Is...>) {
+  (body(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& body) {
+  static_for(static_cast<F&&>(body), std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ u32x4_t lds16(const char* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }

@@ -641,3 +641,53 @@ def test_cu_budget_gives_identical_results(budget):
         _, _, o_ref = oracle.muon_step(np.zeros_like(gh), gh, mh, lr=wl.lr, beta=wl.beta, steps=5)
         o_step = -host_f64(wz[i]) / update_step(*sh, wl.lr)
         check_blocks(o_step, o_ref, TOL["bf16"], what=f"step O, budget {budget}, {sh}")
+
+
+def _up(x, a):
+    return -(-x // a) * a
+
+
+def _workspace_sym(ws, shape):
+    """A = X X^T and B = c A^2 + b A of the only matrix of a one-matrix bf16 call,
+    read from the workspace (layout in muon_internal.hpp: descriptor table, the 7
+    phase prefix arrays, the inverse norm, the momentum-pass partials, X ping,
+    X pong, A, B; matrices in 256 x 32 slabs) as s_pad x s_pad int16 arrays."""
+    r, c = shape
+    tall = r > c
+    sp, lp = _up(min(shape), 256), _up(max(shape), 256)
+    blocks = (sp // 256) * (lp // 64) if tall else (sp // 32) * (lp // 256)
+    off = _up(112, 256) + _up(4 * 7 * 2, 256) + _up(4, 256) + _up(4 * blocks, 256)
+    off += 2 * _up(sp * lp * 2, 256)
+    raw = ws.view(torch.int16)
+    out = []
+    for k in range(2):
+        n = sp * sp
+        slabs = raw[off // 2:off // 2 + n].cpu().numpy().reshape(sp // 256, sp // 32, 256, 32)
+        out.append(slabs.transpose(0, 2, 1, 3).reshape(sp, sp))
+        off += _up(n * 2, 256)
+    return out
+
+
+@pytest.mark.parametrize("shape", [(300, 700), (1040, 520), (1536, 1600)])
+def test_gram_and_square_are_exactly_symmetric(shape):
+    """The stored A and B are bitwise symmetric: off-diagonal tiles store their
+    mirror, and diagonal tiles form only the blocks on and above the diagonal and
+    mirror them.  Also each is within the bf16 tolerance of the oracle's A and
+    c A^2 + b A of the first step."""
+    x = torch.from_numpy(np.random.default_rng(11).standard_normal(shape).astype(np.float32))
+    x = x.to(torch.bfloat16).cuda()
+    ws = nsa.allocate_workspace([shape], torch.bfloat16, "cuda")
+    nsa.ns_batched([x], steps=1, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = _workspace_sym(ws, shape)
+    assert np.array_equal(a, a.T) and np.array_equal(b, b.T)
+    u = host_f64(x)
+    u = u.T if shape[0] > shape[1] else u
+    x0 = u / (np.linalg.norm(u) + 1e-7)
+    s = x0.shape[0]
+    _, qb, qc = oracle.QUINTIC
+    a_ref = x0 @ x0.T
+    b_ref = qc * (a_ref @ a_ref) + qb * a_ref
+    bf = lambda v: torch.from_numpy(v.astype(np.int16)).view(torch.bfloat16).double().numpy()
+    check_blocks(bf(a)[:s, :s], a_ref, TOL["bf16"], what=f"A {shape}")
+    check_blocks(bf(b)[:s, :s], b_ref, TOL["bf16"], what=f"B {shape}")
