@@ -36,13 +36,15 @@
  *  - The caller owns every buffer, the workspace included.  The library
  *    allocates no device memory and keeps no pointer after it returns; it owns
  *    only a pool of small pinned host staging buffers for the descriptor
- *    upload, allocated on first use and kept until the process ends.  A call
- *    takes a staging buffer whose upload has completed, or a new one when all
- *    are in flight (at most 256 per device).
+ *    upload, allocated on first use and kept until the process ends, and, once
+ *    a step with momentum_host = 1 has run on a device, two copy streams and
+ *    their events there.  A call takes a staging buffer whose upload has
+ *    completed, or a new one when all are in flight (at most 256 per device).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream)
  *    and the call returns without waiting for the GPU, except with more than
  *    256 calls in flight on one device, when it waits for the oldest one's
- *    descriptor upload.  Buffers must stay alive and untouched until the
+ *    descriptor upload, and for a step with momentum_host = 1, which first
+ *    waits for the previous such step on the device (see muon_step_params).  Buffers must stay alive and untouched until the
  *    stream has finished the work.  Two calls may run concurrently only with
  *    distinct workspaces.
  *  - Every argument is validated before anything is enqueued; on any error

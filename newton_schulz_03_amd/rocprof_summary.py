@@ -39,8 +39,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # Sources that set the matrix-core kernels' memory traffic: their device code,
 # and the host code that cuts each launch's tiles into per-XCD ranges (which
 # tiles share an L2).
-KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_common.hpp", "csrc/device_common.hpp",
-                  "csrc/muon_internal.hpp", "csrc/muon_abi.hip")
+KERNEL_SOURCES = ("csrc/gemm_bf16.hip", "csrc/gemm_pipeline.hpp", "csrc/gemm_common.hpp",
+                  "csrc/device_common.hpp", "csrc/muon_internal.hpp", "csrc/muon_abi.hip")
 
 # The wide-tile products (256 x 384 tiles) take the labels of the products they
 # replace: a call uses one kind or the other for all of its middle products.
