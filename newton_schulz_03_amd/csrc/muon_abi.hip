@@ -626,6 +626,7 @@ struct CopyStreams {
   hipStream_t in = nullptr, out = nullptr;
   hipEvent_t start = nullptr;
   hipEvent_t in_done[kMaxChunks], prep_done[kMaxChunks], out_done[kMaxChunks];
+  hipEvent_t in_end = nullptr, out_end = nullptr;  // the join of a call
   hipEvent_t done = nullptr;  // the end of the last call
   bool pending = false;       // done has been recorded
   std::mutex mu;  // one chunked call enqueues at a time on a device
@@ -649,7 +650,9 @@ int32_t copy_streams(CopyStreams** out) {
       (e = hipEventCreateWithFlags(&cs->start, hipEventDisableTiming)) != hipSuccess)
     return hip_fail(e, "creating the copy streams");
   if ((e = hipEventCreateWithFlags(&cs->done, hipEventDisableTiming | hipEventBlockingSync)) !=
-      hipSuccess)
+          hipSuccess ||
+      (e = hipEventCreateWithFlags(&cs->in_end, hipEventDisableTiming)) != hipSuccess ||
+      (e = hipEventCreateWithFlags(&cs->out_end, hipEventDisableTiming)) != hipSuccess)
     return hip_fail(e, "creating the copy events");
   for (int k = 0; k < kMaxChunks; ++k) {
     if ((e = hipEventCreateWithFlags(&cs->in_done[k], hipEventDisableTiming)) != hipSuccess ||
@@ -687,43 +690,53 @@ int32_t run_chunked(ChunkPlan& cp, char* ws, hipStream_t user, const ElemParams&
       !ok(hipStreamWaitEvent(cs->out, cs->start, 0), "hipStreamWaitEvent"))
     return st;
   const int nchunks = static_cast<int>(cp.plans.size());
-  for (int k = 0; k < nchunks; ++k) {
-    const int32_t a = cp.first[k], b = cp.first[k + 1];
-    char* slot = ws + cp.staging_off + static_cast<size_t>(k & 1) * cp.staging_bytes;
-    // copy in, once the slot's previous chunk has gone back to the host
-    if (k >= 2 && !ok(hipStreamWaitEvent(cs->in, cs->out_done[k - 2], 0), "hipStreamWaitEvent"))
-      return st;
-    for (int32_t i = a; i < b; ++i)
-      if (!ok(hipMemcpyAsync(slot + cp.stage_off[i], m[i], cp.bytes[i], hipMemcpyHostToDevice,
-                             cs->in), "hipMemcpyAsync (momentum to the device)"))
+  auto chunks = [&]() -> int32_t {
+    for (int k = 0; k < nchunks; ++k) {
+      const int32_t a = cp.first[k], b = cp.first[k + 1];
+      char* slot = ws + cp.staging_off + static_cast<size_t>(k & 1) * cp.staging_bytes;
+      // copy in, once the slot's previous chunk has gone back to the host
+      if (k >= 2 && !ok(hipStreamWaitEvent(cs->in, cs->out_done[k - 2], 0), "hipStreamWaitEvent"))
         return st;
-    if (!ok(hipEventRecord(cs->in_done[k], cs->in), "hipEventRecord")) return st;
-    // the chunk's step, on the caller's stream
-    Plan& pl = cp.plans[k];
-    char* wsk = ws + cp.ws_off[k];
-    bind(pl, wsk);
-    for (int32_t i = a; i < b; ++i) {
-      MatDesc& d = pl.desc[i - a];
-      d.src = g[i];
-      d.dst = w[i];
-      d.mom = slot + cp.stage_off[i];
+      for (int32_t i = a; i < b; ++i)
+        if (!ok(hipMemcpyAsync(slot + cp.stage_off[i], m[i], cp.bytes[i], hipMemcpyHostToDevice,
+                               cs->in), "hipMemcpyAsync (momentum to the device)"))
+          return st;
+      if (!ok(hipEventRecord(cs->in_done[k], cs->in), "hipEventRecord")) return st;
+      // the chunk's step, on the caller's stream
+      Plan& pl = cp.plans[k];
+      char* wsk = ws + cp.ws_off[k];
+      bind(pl, wsk);
+      for (int32_t i = a; i < b; ++i) {
+        MatDesc& d = pl.desc[i - a];
+        d.src = g[i];
+        d.dst = w[i];
+        d.mom = slot + cp.stage_off[i];
+      }
+      if (!ok(hipStreamWaitEvent(user, cs->in_done[k], 0), "hipStreamWaitEvent")) return st;
+      if ((st = put_table(pl, wsk, user)) != MUON_OK) return st;
+      if ((st = run(pl, wsk, user, ep, ns, true, cs->prep_done[k])) != MUON_OK) return st;
+      // copy back, as soon as the momentum pass is done
+      if (!ok(hipStreamWaitEvent(cs->out, cs->prep_done[k], 0), "hipStreamWaitEvent")) return st;
+      for (int32_t i = a; i < b; ++i)
+        if (!ok(hipMemcpyAsync(m[i], slot + cp.stage_off[i], cp.bytes[i], hipMemcpyDeviceToHost,
+                               cs->out), "hipMemcpyAsync (momentum to the host)"))
+          return st;
+      if (!ok(hipEventRecord(cs->out_done[k], cs->out), "hipEventRecord")) return st;
     }
-    if (!ok(hipStreamWaitEvent(user, cs->in_done[k], 0), "hipStreamWaitEvent")) return st;
-    if ((st = put_table(pl, wsk, user)) != MUON_OK) return st;
-    if ((st = run(pl, wsk, user, ep, ns, true, cs->prep_done[k])) != MUON_OK) return st;
-    // copy back, as soon as the momentum pass is done
-    if (!ok(hipStreamWaitEvent(cs->out, cs->prep_done[k], 0), "hipStreamWaitEvent")) return st;
-    for (int32_t i = a; i < b; ++i)
-      if (!ok(hipMemcpyAsync(m[i], slot + cp.stage_off[i], cp.bytes[i], hipMemcpyDeviceToHost,
-                             cs->out), "hipMemcpyAsync (momentum to the host)"))
-        return st;
-    if (!ok(hipEventRecord(cs->out_done[k], cs->out), "hipEventRecord")) return st;
-  }
-  if (!ok(hipStreamWaitEvent(user, cs->out_done[nchunks - 1], 0), "hipStreamWaitEvent") ||
-      !ok(hipEventRecord(cs->done, user), "hipEventRecord"))
-    return st;
-  cs->pending = true;
-  return MUON_OK;
+    return MUON_OK;
+  };
+  const int32_t body = chunks();
+  // The join, also after an error part-way (so that nothing this call enqueued
+  // on the copy streams runs unordered with the caller's later work): the
+  // caller's stream waits for the last work of both copy streams.
+  const bool joined = ok(hipEventRecord(cs->in_end, cs->in), "hipEventRecord") &&
+                      ok(hipEventRecord(cs->out_end, cs->out), "hipEventRecord") &&
+                      ok(hipStreamWaitEvent(user, cs->in_end, 0), "hipStreamWaitEvent") &&
+                      ok(hipStreamWaitEvent(user, cs->out_end, 0), "hipStreamWaitEvent") &&
+                      ok(hipEventRecord(cs->done, user), "hipEventRecord");
+  if (joined) cs->pending = true;
+  if (body != MUON_OK) return body;
+  return joined ? MUON_OK : st;
 }
 
 }  // namespace
