@@ -11,6 +11,8 @@
 //   - the tile orders (prod_tile, sym_tile) take every tile of a grid once.
 //   - the wide product tiles (256 x kTileW) are planned exactly when every
 //     padded long side is a multiple of kTileW, in bf16, and split the same way.
+//   - the chunks of a step with the momentum in host memory cover the batch
+//     once, at most kMaxChunks of them, each inside its staging slot.
 // Prints "OK <plans>" and exits 0, or names the first failure and exits 1.
 #include "muon_abi.hip"
 
@@ -173,6 +175,47 @@ int main() {
     expect(pl.wide_prod && pl.split_prodw.grid == 12288, "uniform wide grid", -1);
     for (int x = 0; x <= kXcd; ++x)
       expect(pl.split_prodw.lo[x] == 1536 * x, "uniform wide ranges", -1);
+  }
+  // the chunks of a step with the momentum in host memory: at most kMaxChunks
+  // contiguous chunks covering every matrix once, each chunk's momentum inside
+  // a staging slot, the chunks' workspace parts and the two slots disjoint
+  for (int trial = 0; trial < 300; ++trial) {
+    const int batch = 1 + static_cast<int>(rng() % (trial < 150 ? 40 : 400));
+    std::vector<int64_t> r(batch), c(batch);
+    for (int i = 0; i < batch; ++i) {
+      r[i] = dims[rng() % 12];
+      c[i] = dims[rng() % 12];
+    }
+    const int32_t dtype = (trial & 1) ? MUON_FP32 : MUON_BF16;
+    const size_t esize = dtype == MUON_BF16 ? 2 : 4;
+    ChunkPlan cp;
+    if (make_chunks(batch, r.data(), c.data(), dtype, trial % 3 == 0 && dtype == MUON_BF16, cp) !=
+        MUON_OK) {
+      expect(false, "make_chunks failed", trial);
+      continue;
+    }
+    const int nchunks = static_cast<int>(cp.plans.size());
+    expect(nchunks >= 1 && nchunks <= kMaxChunks, "chunk count out of range", trial);
+    expect(cp.first.size() == static_cast<size_t>(nchunks) + 1 && cp.first[0] == 0 &&
+               cp.first[nchunks] == batch, "chunks do not span the batch", trial);
+    size_t part_end = 0;
+    for (int k = 0; k < nchunks; ++k) {
+      expect(cp.first[k + 1] > cp.first[k], "an empty chunk", trial);
+      expect(cp.plans[k].batch == cp.first[k + 1] - cp.first[k], "chunk plan size", trial);
+      expect(cp.ws_off[k] == part_end && cp.ws_off[k] % kAlign == 0, "chunk parts not packed", trial);
+      part_end = cp.ws_off[k] + align_up(cp.plans[k].total_bytes, kAlign);
+      size_t slot_end = 0;
+      for (int32_t i = cp.first[k]; i < cp.first[k + 1]; ++i) {
+        expect(cp.bytes[i] == esize * static_cast<size_t>(r[i] * c[i]), "momentum bytes", trial);
+        expect(cp.stage_off[i] == slot_end && cp.stage_off[i] % kAlign == 0,
+               "momentum not packed in its slot", trial);
+        slot_end = cp.stage_off[i] + align_up(cp.bytes[i], kAlign);
+      }
+      expect(slot_end <= cp.staging_bytes, "a chunk overflows its staging slot", trial);
+    }
+    expect(cp.staging_off == part_end, "slots do not follow the parts", trial);
+    expect(cp.total_bytes == cp.staging_off + 2 * cp.staging_bytes, "total bytes", trial);
+    ++plans;
   }
   // an empty batch launches nothing
   {
