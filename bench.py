@@ -736,8 +736,20 @@ def main(argv=None) -> int:
         "per_kernel_pass_ms_per_step": round(instrumented_ms, 3),
         "kernels": per_kernel,
     }
-    if nchunks > 1:
+    if args.momentum_host:
+        # the DMA copies, timed by the library on its copy streams: how much of
+        # them the step hides behind the Newton-Schulz kernels
+        in_ms, out_ms = kern["mom_in"][0] / args.steps, kern["mom_out"][0] / args.steps
+        gpu_ms = sum(kern[k][0] for k in nsa.KERNELS if not k.startswith("mom_")) / args.steps
+        mbytes = sum(esize * r * c for r, c in shapes)
         result["momentum_chunks"] = nchunks
+        result["momentum_copies"] = {
+            "to_device_ms_per_step": round(in_ms, 3), "to_host_ms_per_step": round(out_ms, 3),
+            "to_device_gbs": round(mbytes / (in_ms * 1e-3) / 1e9, 1),
+            "to_host_gbs": round(mbytes / (out_ms * 1e-3) / 1e9, 1),
+            "kernels_ms_per_step": round(gpu_ms, 3),
+            "serial_ms_per_step": round(in_ms + out_ms + gpu_ms, 3),
+            "measured_ms_per_step": round(instrumented_ms, 3)}
     if args.copy_calibration_mb > 0:
         # one plain copy of known size (reads n bytes, writes n bytes): hardware
         # traffic counters of the same run are scaled by what they read for it

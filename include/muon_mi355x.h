@@ -269,7 +269,8 @@ int32_t muon_adamw_batched(int32_t batch, const int64_t* numel, void* const* p,
                            const muon_adamw_params* params, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Kernels of the step, for per-kernel timing. */
+/* Kernels of the step, and the momentum copies of a step with the momentum in
+ * host memory, for per-kernel timing. */
 typedef enum {
   MUON_K_PREPARE = 0,   /* momentum, U into the iterate (short side first), sums of squares */
   MUON_K_NORM = 1,      /* 1 / (||U||_F + eps) per matrix */
@@ -284,12 +285,15 @@ typedef enum {
   MUON_K_GRAM8 = 10,      /* e4m3 steps: A = X X^T */
   MUON_K_POLY8 = 11,      /* e4m3 steps: B = b A + c A^2 */
   MUON_K_PROD8 = 12,      /* e4m3 steps: X <- a X + B X */
-  MUON_K_COUNT = 13
+  MUON_K_MOM_IN = 13,     /* momentum_host: one chunk's momentum copied to the device (DMA) */
+  MUON_K_MOM_OUT = 14,    /* momentum_host: one chunk's momentum copied back to the host (DMA) */
+  MUON_K_COUNT = 15
 } muon_kernel;
 
 /*
  * Per-kernel timing, off by default.  While enabled (process-wide), every call
- * records a pair of HIP events on its stream around each kernel launch.
+ * records a pair of HIP events on its stream around each kernel launch (and, with
+ * the momentum in host memory, on the copy streams around each chunk's copies).
  * muon_timing_read waits for the recorded events, adds their elapsed times to
  * per-kernel totals, and returns the total milliseconds and the number of
  * launches of `kernel` since the last muon_timing_reset.  Returns MUON_OK,

@@ -30,7 +30,7 @@ EXPORTED = ("muon_workspace_bytes", "muon_workspace_bytes_ex", "muon_ns_batched"
             "muon_status_string", "muon_last_error_detail", "muon_timing_enable",
             "muon_timing_read", "muon_timing_reset", "muon_hbm_stream")
 KERNELS = ("prepare", "norm", "gram", "poly", "prod", "finish", "adamw", "prod_finish", "prod_first",
-           "quant8", "gram8", "poly8", "prod8")
+           "quant8", "gram8", "poly8", "prod8", "mom_in", "mom_out")
 
 
 class MuonError(RuntimeError):

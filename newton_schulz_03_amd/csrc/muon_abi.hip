@@ -697,10 +697,14 @@ int32_t run_chunked(ChunkPlan& cp, char* ws, hipStream_t user, const ElemParams&
       // copy in, once the slot's previous chunk has gone back to the host
       if (k >= 2 && !ok(hipStreamWaitEvent(cs->in, cs->out_done[k - 2], 0), "hipStreamWaitEvent"))
         return st;
-      for (int32_t i = a; i < b; ++i)
-        if (!ok(hipMemcpyAsync(slot + cp.stage_off[i], m[i], cp.bytes[i], hipMemcpyHostToDevice,
-                               cs->in), "hipMemcpyAsync (momentum to the device)"))
-          return st;
+      {
+        TimedLaunch t(MUON_K_MOM_IN, cs->in);
+        for (int32_t i = a; i < b; ++i)
+          if (!ok(hipMemcpyAsync(slot + cp.stage_off[i], m[i], cp.bytes[i], hipMemcpyHostToDevice,
+                                 cs->in), "hipMemcpyAsync (momentum to the device)"))
+            return st;
+        t.done();
+      }
       if (!ok(hipEventRecord(cs->in_done[k], cs->in), "hipEventRecord")) return st;
       // the chunk's step, on the caller's stream
       Plan& pl = cp.plans[k];
@@ -717,10 +721,14 @@ int32_t run_chunked(ChunkPlan& cp, char* ws, hipStream_t user, const ElemParams&
       if ((st = run(pl, wsk, user, ep, ns, true, cs->prep_done[k])) != MUON_OK) return st;
       // copy back, as soon as the momentum pass is done
       if (!ok(hipStreamWaitEvent(cs->out, cs->prep_done[k], 0), "hipStreamWaitEvent")) return st;
-      for (int32_t i = a; i < b; ++i)
-        if (!ok(hipMemcpyAsync(m[i], slot + cp.stage_off[i], cp.bytes[i], hipMemcpyDeviceToHost,
-                               cs->out), "hipMemcpyAsync (momentum to the host)"))
-          return st;
+      {
+        TimedLaunch t(MUON_K_MOM_OUT, cs->out);
+        for (int32_t i = a; i < b; ++i)
+          if (!ok(hipMemcpyAsync(m[i], slot + cp.stage_off[i], cp.bytes[i], hipMemcpyDeviceToHost,
+                                 cs->out), "hipMemcpyAsync (momentum to the host)"))
+            return st;
+        t.done();
+      }
       if (!ok(hipEventRecord(cs->out_done[k], cs->out), "hipEventRecord")) return st;
     }
     return MUON_OK;
