@@ -691,3 +691,29 @@ def test_gram_and_square_are_exactly_symmetric(shape):
     bf = lambda v: torch.from_numpy(v.astype(np.int16)).view(torch.bfloat16).double().numpy()
     check_blocks(bf(a)[:s, :s], a_ref, TOL["bf16"], what=f"A {shape}")
     check_blocks(bf(b)[:s, :s], b_ref, TOL["bf16"], what=f"B {shape}")
+
+
+def test_launch_sequence_momentum_host():
+    """A step with the momentum in host memory runs the step's kernels once per
+    chunk, and copies each chunk's momentum in and out once (timed on the copy
+    streams)."""
+    shapes = [(300, 700), (700, 300), (256, 512), (512, 256), (640, 640)]
+    wl = _wl("muon", "bf16", shapes)
+    ins = device_inputs(wl)
+    m_host = [d["m"].cpu().pin_memory() for d in ins]
+    ws = nsa.allocate_workspace(shapes, torch.bfloat16, "cuda", momentum_host=True)
+    torch.cuda.synchronize()
+    nsa.timing_reset()
+    nsa.timing_enable(True)
+    try:
+        nsa.step_batched([d["w"] for d in ins], [d["g"] for d in ins], m_host, steps=2,
+                         workspace=ws, momentum_host=True)
+        torch.cuda.synchronize()
+    finally:
+        nsa.timing_enable(False)
+    got = {k: n for k, (_, n) in nsa.timing_read().items() if n}
+    chunks = got["prepare"]
+    assert 1 < chunks <= 16, got
+    want = {"prepare": chunks, "norm": chunks, "gram": 2 * chunks, "poly": 2 * chunks,
+            "prod_first": chunks, "prod_finish": chunks, "mom_in": chunks, "mom_out": chunks}
+    assert got == want
