@@ -5,8 +5,8 @@ library's own scratch array, so its outputs must equal the workspace call's bit
 for bit, and each must be within the tolerance of the oracle per 256 x 256
 block.  Two calls in a row, the second over smaller matrices (the array keeps
 the first call's contents, which the second must not depend on), in bf16 and
-fp32; and a batch too large for the array is refused without touching the
-outputs.
+fp32, and with e4m3 steps; and a batch too large for the array is refused
+without touching the outputs.
 """
 import numpy as np
 import pytest
@@ -48,6 +48,19 @@ def test_noalloc_equals_workspace_call(dtype):
             assert torch.equal(got[i], ref[i]), (dtype, call, sh)
             check_blocks(host_f64(got[i]), oracle.newton_schulz(host_f64(xs[i]), 5), TOL[dtype],
                          what=f"noalloc {dtype} call {call} {sh}")
+
+
+def test_noalloc_with_e4m3_steps():
+    """The e4m3 steps on the library's array (its e4m3 buffers included) equal
+    the workspace call's, two calls in a row, the second smaller."""
+    for call, shapes in enumerate((FIRST, SECOND)):
+        xs = _inputs(shapes, "bf16", 200 + call)
+        ref = nsa.ns_batched(xs, steps=5, fp8_steps=2)
+        got = [torch.full_like(x, 7.0) for x in xs]
+        nsa.ns_batched_noalloc(xs, got, steps=5, fp8_steps=2)
+        torch.cuda.synchronize()
+        for i, sh in enumerate(shapes):
+            assert torch.equal(got[i], ref[i]), (call, sh)
 
 
 def test_noalloc_in_stream_order_and_too_large():
