@@ -10,7 +10,10 @@ workload is 96 bf16 expert matrices of 2048 x 6144.  Prints one JSON line.
 The headline is timed with HIP events around the K steps alone, with the
 library's per-kernel instrumentation off.  The per-kernel durations come from a
 second pass of K steps in which the library records HIP events around each
-launch, on the stream the kernels run on.
+launch, on the stream the kernels run on.  After them, on the same inputs,
+"variants" times the step with e4m3 operands in the first two Newton-Schulz
+steps and with the momentum in pinned host memory (not the headline; skipped
+with --no-variants).
 
     python bench.py --hbm-ceiling
 
@@ -262,6 +265,47 @@ def bench_hbm_ceiling(args) -> int:
                       "unit": "GB/s", "bytes_per_stream": n, "peak": PEAK_HBM_GBS,
                       "median_of": args.steps, "patterns": out}), flush=True)
     return 0
+
+
+def bench_variants(args, wl, W, G, M, shapes, dev) -> dict:
+    """The same step with its two options, after the headline and on the same
+    inputs: e4m3 operands in the first two Newton-Schulz steps, and the
+    momentum in pinned host memory.  Each: `warmup` untimed steps, then `steps`
+    timed ones; not the headline (another dtype, or another memory)."""
+    import torch
+
+    import newton_schulz_03_amd as nsa
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize(dev)
+        return a.elapsed_time(b) / args.steps
+
+    kw = dict(lr=wl.lr, beta=wl.beta, nesterov=wl.nesterov, steps=wl.steps, coeffs=wl.coeffs,
+              eps=wl.eps)
+    out = {}
+    ws8 = nsa.allocate_workspace(shapes, torch.bfloat16, dev, fp8=True)
+    ms = timed(lambda: nsa.step_batched(W, G, M, workspace=ws8, fp8_steps=2, **kw))
+    out["fp8_steps_2"] = {"ms_per_step": round(ms, 3), "value": round(wl.batch / ms * 1e3, 2),
+                          "unit": "matrices/s", "dtype": "bf16+e4m3"}
+    print(f"[bench] variant e4m3 steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    del ws8
+    mh = [m.cpu().pin_memory() for m in M]
+    wsh = nsa.allocate_workspace(shapes, torch.bfloat16, dev, momentum_host=True)
+    ms = timed(lambda: nsa.step_batched(W, G, mh, workspace=wsh, momentum_host=True, **kw))
+    out["momentum_host"] = {"ms_per_step": round(ms, 3), "value": round(wl.batch / ms * 1e3, 2),
+                            "unit": "matrices/s", "momentum": "pinned host memory"}
+    print(f"[bench] variant momentum in host memory: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    del wsh, mh
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_link_ceiling(args) -> int:
@@ -564,6 +608,8 @@ def main(argv=None) -> int:
     ap.add_argument("--blas-compare", action="store_true",
                     help="time the vendor library's batched GEMM on the step's products beside "
                          "this library's kernels")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the step's e4m3 and host-momentum variants after the headline")
     ap.add_argument("--link-ceiling", action="store_true",
                     help="measure the host link with plain DMA copies of the momentum's size")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -750,6 +796,9 @@ def main(argv=None) -> int:
             "kernels_ms_per_step": round(gpu_ms, 3),
             "serial_ms_per_step": round(in_ms + out_ms + gpu_ms, 3),
             "measured_ms_per_step": round(instrumented_ms, 3)}
+    if (not args.no_variants and wl.call == "step" and wl.dtype == "bf16" and not args.momentum_host
+            and args.fp8_steps == 0):
+        result["variants"] = bench_variants(args, wl, W, G, M, shapes, dev)
     if args.copy_calibration_mb > 0:
         # one plain copy of known size (reads n bytes, writes n bytes): hardware
         # traffic counters of the same run are scaled by what they read for it
