@@ -8,7 +8,8 @@
 //   - split_tile (the function the kernels call) maps the grid's workgroups
 //     onto every tile exactly once, the rest to -1;
 //   - every XCD's range holds at most 1/8 of the launch's work plus one tile.
-//   - the tile orders (prod_tile, sym_tile) take every tile of a grid once.
+//   - the tile orders (prod_tile, sym_tile) take every tile of a grid once, and
+//     sym_tile takes the diagonal tiles of each band of kTileGroup rows in a row.
 //   - the wide product tiles (256 x kTileW) are planned exactly when every
 //     padded long side is a multiple of kTileW, in bf16, and split the same way.
 //   - the chunks of a step with the momentum in host memory cover the batch
@@ -164,6 +165,18 @@ int main() {
     for (int32_t i = 0; i < ts; ++i)
       for (int32_t jj = i; jj < ts; ++jj)
         expect(seen[static_cast<size_t>(i) * ts + jj] == 1, "sym_tile does not take every tile once", ts);
+    // the diagonal tiles of a band are consecutive, in row order
+    for (int32_t a = 0; a < ts; a += kTileGroup) {
+      int32_t first = -1;
+      for (int32_t t = 0; t < ts * (ts + 1) / 2; ++t) {
+        int32_t ti = -1, tj = -1;
+        sym_tile(t, ts, ti, tj);
+        if (ti == tj && ti >= a && ti < a + kTileGroup) {
+          if (first < 0) first = t;
+          expect(t == first + (ti - a), "sym_tile: the diagonal tiles of a band are not in a row", ts);
+        }
+      }
+    }
   }
   // a uniform batch keeps equal ranges and one workgroup per tile
   {
