@@ -52,7 +52,10 @@
  *    that returns MUON_OK.
  *  - NaN and Inf propagate; there is no check.  A zero input gives a zero
  *    output (eps keeps the normalization finite).
- *  - Results are deterministic: the kernels use no floating-point atomics.
+ *  - Results are deterministic: the kernels use no floating-point atomics.  The
+ *    matrix-core launches hand out the last tiles of each XCD's share with
+ *    integer atomics on counters in the workspace, to whichever XCD is free;
+ *    which CU computes a tile never changes its value.
  *  - No C++ exception crosses this interface.
  *
  * Precision.  MUON_BF16: tensors are bf16; products accumulate in fp32 on the

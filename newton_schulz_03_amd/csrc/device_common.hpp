@@ -123,6 +123,25 @@ __device__ __forceinline__ void* iterate(const MatDesc& d, int which) {
   return which ? d.x[1] : d.x[0];
 }
 
+// A value from a table that no kernel writes while it runs (the descriptors,
+// the block prefixes), read through the constant address space.  The matrix-
+// core kernels write memory before they read these tables (the atomics of a
+// tile claim); through a generic pointer the compiler then no longer proves the
+// table unchanged and loads it into vector registers instead of scalar ones,
+// which made the wide product kernel spill 82 registers inside its K loop.
+template <typename T>
+__device__ __forceinline__ T load_const(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "whole dwords");
+  using CU32 = const __attribute__((address_space(4))) uint32_t;
+  CU32* q = (CU32*)(p);
+  uint32_t w[sizeof(T) / 4];
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(T) / 4); ++i) w[i] = q[i];
+  T v;
+  __builtin_memcpy(&v, w, sizeof(T));
+  return v;
+}
+
 // Index j with prefix[j] <= b < prefix[j+1] (b < prefix[batch]); exactly one
 // interval holds b, and empty intervals never match.  Up to kLocateScan
 // matrices the whole block finds it at once: every thread tests a few
@@ -139,7 +158,7 @@ __device__ __forceinline__ int locate_matrix(const int32_t* prefix, int batch, i
     int lo = 0, hi = batch;  // prefix[lo] <= b < prefix[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (prefix[mid] <= b)
+      if (load_const(prefix + mid) <= b)
         lo = mid;
       else
         hi = mid;

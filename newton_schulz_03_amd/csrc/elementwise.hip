@@ -257,11 +257,17 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
 
 // ---------------------------------------------------------------------------
 // k_finalize: block j sums matrix j's partials in a fixed order (double), then
-// stores 1 / (sqrt(sum) + eps).
+// stores 1 / (sqrt(sum) + eps).  Block 0 also zeroes both sets of claim
+// counters, ahead of the call's first matrix-core launch.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_finalize(LaunchCtx c, ElemParams p) {
   __shared__ double scratch[kThreads / 64];
   const int j = blockIdx.x;
+  if (j == 0 && threadIdx.x < 2 * kSchedInts) {
+    int32_t* set = threadIdx.x < kSchedInts ? c.sched : c.sched_next;
+    __hip_atomic_store(set + (threadIdx.x % kSchedInts), 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
   const int32_t* pre = c.prefix + PH_PREPARE * (c.batch + 1);
   double s = 0.0;
   for (int32_t k = pre[j] + threadIdx.x; k < pre[j + 1]; k += kThreads) s += c.partials[k];

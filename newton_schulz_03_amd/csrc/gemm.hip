@@ -108,9 +108,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_staged(LaunchCtx c, GemmAr
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   constexpr int BK = kRowBytes / sizeof(T);
 
-  __shared__ int slot;
-  const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
-  if (t < 0) return;  // the whole block: t depends on blockIdx.x only
+  __shared__ int slot, claimed;
+  const int32_t t = claim_tile(g.split, c, &claimed);
+  if (t < 0) return;  // the whole block
   const TileRef tr = decode_tile<MODE>(c, t, &slot);
   const MatDesc& d = tr.d;
   const int32_t ti = tr.ti, tj = tr.tj;

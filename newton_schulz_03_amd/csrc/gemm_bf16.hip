@@ -608,9 +608,9 @@ __device__ __forceinline__ TileRef decode_wide(const LaunchCtx& c, int32_t b, in
   const int32_t* pre = c.prefix + PH_PRODW * (c.batch + 1);
   const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;
-  r.d = c.desc[j];
+  r.d = load_const(c.desc + j);
   r.mat = j;
-  prod_tile(b - pre[j], r.d.s_pad / kTile, r.d.l_pad / kTileW, r.ti, r.tj);
+  prod_tile(b - load_const(pre + j), r.d.s_pad / kTile, r.d.l_pad / kTileW, r.ti, r.tj);
   return r;
 }
 
@@ -849,8 +849,8 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
   store_wide(acc, accv, tr, g, nf, smem, wave, lane);
 }
 
-// One block per CU, one tile per block, taken by split_tile: the XCDs get
-// ranges of equal work.  LOOP (a CU budget: fewer workgroups than tiles): a
+// One block per CU, one tile per block, taken by claim_tile: the XCDs get
+// ranges of equal work, the last tiles of each claimed at run time.  LOOP (a CU budget: fewer workgroups than tiles): a
 // block takes tiles blockIdx.x, blockIdx.x + gridDim.x, ..., renumbered so that
 // each XCD walks one contiguous range of equal length.  The loop is a separate
 // instantiation: across tiles the compiler keeps tile-invariant values in
@@ -860,13 +860,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
   __shared__ __attribute__((aligned(1024))) char smem[LDSB];
   __shared__ int slot;
   if constexpr (LOOP) {
+    zero_next_sched(c);
     for (int32_t v = blockIdx.x; v < g.ntiles; v += gridDim.x) {
       gemm_tile<MODE, FINAL, FIRST, true>(c, g, xcd_remap(v, g.ntiles), smem, &slot);
       __syncthreads();  // every wave is done with LDS before the next tile's loads land there
     }
   } else {
-    const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
-    if (t < 0) return;  // the whole block: t depends on blockIdx.x only
+    __shared__ int claimed;
+    const int32_t t = claim_tile(g.split, c, &claimed);
+    if (t < 0) return;  // the whole block
     gemm_tile<MODE, FINAL, FIRST, false>(c, g, t, smem, &slot);
   }
 }
@@ -881,15 +883,17 @@ void launch_one(const LaunchCtx& c, int32_t nblocks, bool loop, const GemmArgs& 
                        c.stream, c, g);
 }
 
-// Wide product tiles, one per workgroup (split_tile).  The matrix lookup's LDS
-// slot sits in the last ring stage, which the prologue leaves unfilled: every
-// wave has read it before the first slice refills that stage.
+// Wide product tiles, one per workgroup (claim_tile).  The LDS slots of the
+// claim and of the matrix lookup sit in the last ring stage, which the
+// prologue leaves unfilled: every wave has read both before the first slice
+// refills that stage.
 template <bool FIRST>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16_wide(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDSW];
-  const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
-  if (t < 0) return;  // the whole block: t depends on blockIdx.x only
-  gemm_tile_wide<FIRST>(c, g, t, smem, reinterpret_cast<int*>(smem + (NST - 1) * STAGEW));
+  int* slots = reinterpret_cast<int*>(smem + (NST - 1) * STAGEW);  // the lookup's, the claim's
+  const int32_t t = claim_tile(g.split, c, slots + 1);
+  if (t < 0) return;  // the whole block
+  gemm_tile_wide<FIRST>(c, g, t, smem, slots);
 }
 
 template <bool FINAL>

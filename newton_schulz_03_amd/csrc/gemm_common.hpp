@@ -39,7 +39,7 @@ struct GemmArgs {
   float lr;           // PROD with FIN_STEP: learning rate
   int32_t first;      // GRAM, PROD: X[cur] holds U; scale by f^2 (GRAM) or f (PROD), f = inv_norm
   int32_t ntiles;     // tiles of the launch
-  XcdSplit split;     // one tile per workgroup: which tile workgroup b takes (split_tile)
+  XcdSplit split;     // one tile per workgroup: which tile workgroup b takes (claim_tile)
 };
 
 template <typename T>
@@ -150,20 +150,99 @@ __device__ __forceinline__ float norm_factor(const LaunchCtx& c, const GemmArgs&
   return MODE == GM_GRAM ? f * f : f;
 }
 
-// Tile of workgroup b in a launch of one tile per workgroup: b runs on XCD
-// x = b % 8 and takes the (b / 8)-th tile of that XCD's range; -1 past its end
-// (the grid covers the longest range, so shorter ones leave workgroups idle).
-__host__ __device__ __forceinline__ int32_t split_tile(const XcdSplit& s, int32_t b) {
-  const int32_t x = b % kXcd, k = b / kXcd;
-  int32_t lo = s.lo[0], hi = s.lo[1];
+// XCD x's range [lo, hi) and the start of its pool [dyn, hi) (an unrolled
+// select: no dynamic index into the kernel argument).
+__host__ __device__ __forceinline__ void xcd_range(const XcdSplit& s, int32_t x, int32_t& lo,
+                                                   int32_t& dyn, int32_t& hi) {
+  lo = s.lo[0];
+  dyn = s.dyn[0];
+  hi = s.lo[1];
 #pragma unroll
   for (int i = 1; i < kXcd; ++i) {
     if (x == i) {
       lo = s.lo[i];
+      dyn = s.dyn[i];
       hi = s.lo[i + 1];
     }
   }
-  return lo + k < hi ? lo + k : -1;
+}
+
+// Statically dealt tile of workgroup b: b runs on XCD x = b % 8 and takes the
+// (b / 8)-th tile of that XCD's range, unless it lies in the range's pool; -1
+// otherwise (the workgroup then claims a pool tile, or finds none left).
+__host__ __device__ __forceinline__ int32_t split_tile(const XcdSplit& s, int32_t b) {
+  const int32_t x = b % kXcd, k = b / kXcd;
+  int32_t lo, dyn, hi;
+  xcd_range(s, x, lo, dyn, hi);
+  return lo + k < dyn ? lo + k : -1;
+}
+
+// Workgroup 0 of a matrix-core launch zeroes the next launch's claim counters
+// (the previous launch's set, which no workgroup uses any more).
+__device__ __forceinline__ void zero_next_sched(const LaunchCtx& c) {
+  if (blockIdx.x == 0 && threadIdx.x < kSchedInts)
+    __hip_atomic_store(c.sched_next + threadIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The tile of this workgroup, or -1.  Called by the whole block (the branch
+// depends on blockIdx.x only); lds is one int of LDS.
+//
+// A workgroup past the static part of its XCD's range claims a pool tile.
+// Wave 0 increments its own XCD's counter: the old value k hands out the k-th
+// tile of that pool.  Once that pool is empty, the wave reads all eight
+// counters and claims from the pool with the most tiles left, and repeats
+// while some pool has tiles.
+//
+// Every increment returns a distinct value, so each pool tile goes to exactly
+// one workgroup.  A workgroup gives up only after reading every pool empty.
+// The grid holds at least as many claiming workgroups as pool tiles.  So every
+// tile is taken exactly once.  A failed claim means that pool emptied after it
+// was read, and it is never picked again: at most kXcd failures, so the loop
+// ends.
+__device__ __forceinline__ int32_t claim_tile(const XcdSplit& s, const LaunchCtx& c, int* lds) {
+  const int32_t b = static_cast<int32_t>(blockIdx.x);
+  zero_next_sched(c);
+  const int32_t t0 = split_tile(s, b);
+  if (t0 >= 0 || s.pool == 0) return t0;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int32_t t = -1;
+    auto claim = [&](int32_t y) {  // lane 0: one increment of pool y's counter
+      if (lane == 0) {
+        int32_t lo, dyn, hi;
+        xcd_range(s, y, lo, dyn, hi);
+        if (dyn < hi) {
+          const int32_t k = atomicAdd(c.sched + y, 1);
+          if (k < hi - dyn) t = dyn + k;
+        }
+      }
+      t = __shfl(t, 0);
+    };
+    claim(b % kXcd);
+    for (int round = 0; t < 0 && round <= kXcd; ++round) {
+      // key = (tiles left) * 8 + (7 - y) on lane y < 8: the largest names the
+      // pool with the most tiles left (the lowest y on a tie)
+      int32_t key = -(1 << 30);
+      if (lane < kXcd) {
+        int32_t lo, dyn, hi;
+        xcd_range(s, lane, lo, dyn, hi);
+        const int32_t taken =
+            __hip_atomic_load(c.sched + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        key = (hi - dyn - taken) * kXcd + (kXcd - 1 - lane);
+      }
+#pragma unroll
+      for (int m = 1; m < kXcd; m <<= 1) key = max(key, __shfl_xor(key, m));
+      key = __shfl(key, 0);
+      if (key < kXcd) break;  // no pool has a tile left
+      claim(kXcd - 1 - (key & (kXcd - 1)));
+    }
+    if (lane == 0) *lds = t;
+  }
+  __syncthreads();
+  // uniform: without readfirstlane the tile and everything derived from it
+  // (matrix, tile row and column, addresses) would sit in vector registers,
+  // and the product kernels spill
+  return __builtin_amdgcn_readfirstlane(*lds);
 }
 
 // Tile number b of the launch -> (matrix, tile) for the symmetric phases (GRAM,
@@ -174,9 +253,9 @@ __device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int32_t b, in
   const int32_t* pre = c.prefix + (MODE == GM_PROD ? PH_PROD : PH_SYM) * (c.batch + 1);
   const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;
-  r.d = c.desc[j];
+  r.d = load_const(c.desc + j);
   r.mat = j;
-  const int32_t t = b - pre[j];
+  const int32_t t = b - load_const(pre + j);
   const int32_t ts = r.d.s_pad / kTile;
   if constexpr (MODE == GM_PROD) {
     prod_tile(t, ts, r.d.l_pad / kTile, r.ti, r.tj);

@@ -247,13 +247,13 @@ __device__ __forceinline__ void gemm_tile_f8(const LaunchCtx& c, const GemmArgs&
 
 }  // namespace
 
-// One block per CU, one tile per block (split_tile: XCD ranges of equal work).
+// One block per CU, one tile per block (claim_tile: XCD ranges of equal work).
 template <int MODE, bool FIRST>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_f8(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDS8];
-  __shared__ int slot;
-  const int32_t t = split_tile(g.split, static_cast<int32_t>(blockIdx.x));
-  if (t < 0) return;  // the whole block: t depends on blockIdx.x only
+  __shared__ int slot, claimed;
+  const int32_t t = claim_tile(g.split, c, &claimed);
+  if (t < 0) return;  // the whole block
   gemm_tile_f8<MODE, FIRST>(c, g, t, smem, &slot);
 }
 

@@ -50,6 +50,7 @@ struct Plan {
   bool fp8 = false;                 // the workspace holds the e4m3 buffers (f8)
   size_t table_bytes = 0;
   size_t inv_off = 0;
+  size_t sched_off = 0;             // two sets of kSchedInts claim counters
   size_t partials_off = 0;
   size_t total_bytes = 0;
 };
@@ -61,6 +62,10 @@ constexpr int64_t kTileOverheadSlices = 12;
 // Cut the tiles of one matrix-core launch into kXcd contiguous ranges of about
 // equal work: XCD x starts at the first tile with at least x/8 of the launch's
 // work before it.  Matrix i contributes cnt[i] tiles of slices[i] K slices.
+// The last 1/16 of each range (at least 8 tiles, a multiple of 8) is claimed at
+// run time, and the grid has as many extra workgroups per XCD: on one chip the
+// XCDs' tile rates differed by up to 7%, and a fixed split waits for the
+// slowest.
 int32_t make_split(const std::vector<int64_t>& cnt, const std::vector<int64_t>& slices,
                    XcdSplit& sp) {
   int64_t total = 0;
@@ -83,9 +88,13 @@ int32_t make_split(const std::vector<int64_t>& cnt, const std::vector<int64_t>& 
   while (x <= kXcd) sp.lo[x++] = static_cast<int32_t>(tiles_before);
   int64_t longest = 0;
   for (x = 0; x < kXcd; ++x) longest = std::max<int64_t>(longest, sp.lo[x + 1] - sp.lo[x]);
-  if (longest * kXcd > 0x7fffffffLL)
+  const int64_t pool = longest == 0 ? 0 : std::max<int64_t>(8, cdiv(cdiv(longest, 16), 8) * 8);
+  if ((longest + pool) * kXcd > 0x7fffffffLL)
     return fail(MUON_ERR_UNSUPPORTED, "batch too large: more than 2^31 blocks in one launch");
-  sp.grid = static_cast<int32_t>(longest * kXcd);
+  sp.pool = static_cast<int32_t>(pool);
+  for (x = 0; x < kXcd; ++x)
+    sp.dyn[x] = sp.lo[x + 1] - static_cast<int32_t>(std::min<int64_t>(pool, sp.lo[x + 1] - sp.lo[x]));
+  sp.grid = static_cast<int32_t>((longest + pool) * kXcd);
   return MUON_OK;
 }
 
@@ -171,6 +180,8 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
   pl.table_bytes = off;
   pl.inv_off = off;
   off += align_up(sizeof(float) * static_cast<size_t>(batch), kAlign);
+  pl.sched_off = off;
+  off += align_up(sizeof(int32_t) * 2 * kSchedInts, kAlign);
   pl.partials_off = off;
   off += align_up(sizeof(float) * static_cast<size_t>(tot[PH_PREPARE]), kAlign);
   for (int32_t i = 0; i < batch; ++i) {
@@ -447,6 +458,18 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   c.prefix = reinterpret_cast<const int32_t*>(ws + align_up(sizeof(MatDesc) * pl.batch, kAlign));
   c.partials = reinterpret_cast<float*>(ws + pl.partials_off);
   c.inv_norm = reinterpret_cast<float*>(ws + pl.inv_off);
+  // claim counters: the finalize kernel zeroes both sets; matrix-core launch i
+  // uses set i % 2 and zeroes the other for launch i + 1
+  int32_t* const sets = reinterpret_cast<int32_t*>(ws + pl.sched_off);
+  c.sched = sets;
+  c.sched_next = sets + kSchedInts;
+  int gemm_launches = 0;
+  auto gemm_ctx = [&]() -> const LaunchCtx& {
+    c.sched = sets + kSchedInts * (gemm_launches & 1);
+    c.sched_next = sets + kSchedInts * ((gemm_launches + 1) & 1);
+    ++gemm_launches;
+    return c;
+  };
   c.batch = pl.batch;
   c.max_blocks = ns.cu_budget;
   c.stream = stream;
@@ -480,7 +503,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
       }
       {
         TimedLaunch t(MUON_K_GRAM8, stream, timed);
-        if ((e = launch_gram8(c, pl.split_gram, use_poly ? 1.f : ns.b, k == 0)) != hipSuccess)
+        if ((e = launch_gram8(gemm_ctx(), pl.split_gram, use_poly ? 1.f : ns.b, k == 0)) != hipSuccess)
           return hip_fail(e, "launch Gram (e4m3)");
         t.done();
       }
@@ -493,7 +516,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
       if (use_poly) {
         {
           TimedLaunch t(MUON_K_POLY8, stream, timed);
-          if ((e = launch_poly8(c, pl.split_poly, ns.b, ns.c)) != hipSuccess)
+          if ((e = launch_poly8(gemm_ctx(), pl.split_poly, ns.b, ns.c)) != hipSuccess)
             return hip_fail(e, "launch polynomial (e4m3)");
           t.done();
         }
@@ -504,7 +527,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
       }
       {
         TimedLaunch t(MUON_K_PROD8, stream, timed);
-        if ((e = launch_prod8(c, pl.split_prod, cur, ns.a, k == 0)) != hipSuccess)
+        if ((e = launch_prod8(gemm_ctx(), pl.split_prod, cur, ns.a, k == 0)) != hipSuccess)
           return hip_fail(e, "launch product (e4m3)");
         t.done();
       }
@@ -513,14 +536,14 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
     }
     {
       TimedLaunch t(MUON_K_GRAM, stream, timed);
-      if ((e = launch_gram(c, pl.split_gram, pl.bf16, cur, use_poly ? 1.f : ns.b, k == 0)) !=
+      if ((e = launch_gram(gemm_ctx(), pl.split_gram, pl.bf16, cur, use_poly ? 1.f : ns.b, k == 0)) !=
           hipSuccess)
         return hip_fail(e, "launch Gram");
       t.done();
     }
     if (use_poly) {
       TimedLaunch t(MUON_K_POLY, stream, timed);
-      if ((e = launch_poly(c, pl.split_poly, pl.bf16, ns.b, ns.c)) != hipSuccess)
+      if ((e = launch_poly(gemm_ctx(), pl.split_poly, pl.bf16, ns.b, ns.c)) != hipSuccess)
         return hip_fail(e, "launch polynomial");
       t.done();
     }
@@ -532,9 +555,9 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
       // wide tiles for the products that store the iterate, unless a CU budget
       // asks for the looping launches (256-wide tiles only)
       if (pl.wide_prod && fin == FIN_NONE && ns.cu_budget == 0) {
-        if ((e = launch_prod_wide(c, pl.split_prodw, cur, ns.a, use_poly, k == 0)) != hipSuccess)
+        if ((e = launch_prod_wide(gemm_ctx(), pl.split_prodw, cur, ns.a, use_poly, k == 0)) != hipSuccess)
           return hip_fail(e, "launch product (wide tiles)");
-      } else if ((e = launch_prod(c, pl.split_prod, pl.bf16, cur, ns.a, use_poly, k == 0, fin,
+      } else if ((e = launch_prod(gemm_ctx(), pl.split_prod, pl.bf16, cur, ns.a, use_poly, k == 0, fin,
                                   ep.lr)) != hipSuccess) {
         return hip_fail(e, "launch product");
       }

@@ -75,16 +75,27 @@ struct MatDesc {
 // Tiles of one matrix-core launch, dealt to the XCDs in contiguous ranges cut
 // so that every XCD gets about the same number of K slices to run, not the
 // same number of tiles: in a ragged batch one tile can cost many times another.
+// The last `pool` tiles of each range are not dealt in advance: workgroups
+// claim them while the launch runs (claim_tile), the XCD's own first, so that
+// an XCD that runs faster than the others ends by taking tiles off theirs.
 struct XcdSplit {
-  int32_t lo[kXcd + 1];  // XCD x takes tiles [lo[x], lo[x + 1]); lo[kXcd] = all tiles
-  int32_t grid;          // kXcd * the longest range: workgroups of a one-tile-each launch
+  int32_t lo[kXcd + 1];  // XCD x owns tiles [lo[x], lo[x + 1]); lo[kXcd] = all tiles
+  int32_t dyn[kXcd];     // its tiles [dyn[x], lo[x + 1]) are claimed at run time
+  int32_t pool;          // the most tiles of one range claimed at run time (0: none)
+  int32_t grid;          // kXcd * (the longest range + pool): the extra workgroups only claim
 };
+
+// Claim counters of the matrix-core launches: kSchedInts int32 per set, two
+// sets used by alternate launches (counter x: tiles claimed from XCD x's pool).
+constexpr int kSchedInts = 16;
 
 struct LaunchCtx {
   const MatDesc* desc;     // device copy of the descriptors
   const int32_t* prefix;   // device: NPHASE arrays of batch+1 block prefixes
   float* partials;         // device: per prepare-block sums of squares
   float* inv_norm;         // device: per matrix 1 / (||U||_F + eps)
+  int32_t* sched;          // device: this matrix-core launch's claim counters (zero at its start)
+  int32_t* sched_next;     // device: the next one's, which this launch zeroes
   int32_t batch;
   int32_t max_blocks;      // matrix-core launches: most workgroups resident (0: one per tile)
   hipStream_t stream;

@@ -4,9 +4,13 @@
 // stub kernel launchers (no kernel is compiled or run).  For ragged batches of
 // random shapes it checks, for the Gram, A^2 and product launches of the plan:
 //   - the ranges start at 0, end at the launch's tile count and never shrink;
-//   - the grid is 8 times the longest range;
-//   - split_tile (the function the kernels call) maps the grid's workgroups
-//     onto every tile exactly once, the rest to -1;
+//   - the grid is 8 times the longest range plus the pool (the tiles at the end
+//     of each range that workgroups claim at run time);
+//   - split_tile (the static part of what the kernels call) maps the grid's
+//     workgroups onto every tile outside the pools exactly once, the rest to -1;
+//   - a model of the run-time claims (random interleavings of the claiming
+//     workgroups' counter reads and increments) hands out every pool tile
+//     exactly once;
 //   - every XCD's range holds at most 1/8 of the launch's work plus one tile.
 //   - the tile orders (prod_tile, sym_tile) take every tile of a grid once, and
 //     sym_tile takes the diagonal tiles of each band of kTileGroup rows in a row.
@@ -69,13 +73,62 @@ void check_split(const XcdSplit& sp, const std::vector<int64_t>& tiles,
     expect(sp.lo[x + 1] >= sp.lo[x], "ranges shrink", plan);
     longest = std::max<int64_t>(longest, sp.lo[x + 1] - sp.lo[x]);
   }
-  expect(sp.grid == kXcd * longest, "grid is not 8 x the longest range", plan);
+  expect(sp.grid == kXcd * (longest + sp.pool), "grid is not 8 x (longest range + pool)", plan);
+  expect(longest == 0 ? sp.pool == 0 : sp.pool >= 8 && sp.pool % 8 == 0 && 16 * sp.pool >= longest,
+         "pool size", plan);
+  for (int x = 0; x < kXcd; ++x)
+    expect(sp.dyn[x] == sp.lo[x + 1] - std::min<int32_t>(sp.pool, sp.lo[x + 1] - sp.lo[x]),
+           "pool start", plan);
   std::vector<int> seen(ntiles, 0);
+  std::vector<int32_t> claimers;
   for (int32_t b = 0; b < sp.grid; ++b) {
     const int32_t t = split_tile(sp, b);
-    if (t == -1) continue;
+    if (t == -1) {
+      claimers.push_back(b);
+      continue;
+    }
     expect(t >= 0 && t < ntiles, "split_tile out of range", plan);
     if (t >= 0 && t < ntiles) seen[t]++;
+  }
+  // the run-time claims, modelled step by step in a random interleaving: a
+  // claimer increments its own XCD's counter; while it has no tile, it reads
+  // every counter (one step) and increments the fullest pool's (the next)
+  std::mt19937 rng(static_cast<uint32_t>(plan) * 7919u + 17u);
+  int32_t cnt[kXcd] = {};
+  struct Claimer { int32_t xcd, state = 0, pick = -1, rounds = 0; bool done = false; };
+  std::vector<Claimer> cl;
+  for (int32_t b : claimers) cl.push_back({b % kXcd});
+  auto take = [&](Claimer&, int32_t y) {
+    int32_t lo, dyn, hi;
+    xcd_range(sp, y, lo, dyn, hi);
+    if (dyn == hi) return false;
+    const int32_t k = cnt[y]++;
+    if (k >= hi - dyn) return false;
+    seen[dyn + k]++;
+    return true;
+  };
+  std::vector<size_t> live(cl.size());
+  for (size_t i = 0; i < live.size(); ++i) live[i] = i;
+  while (!live.empty()) {
+    const size_t li = rng() % live.size();
+    Claimer& c = cl[live[li]];
+    if (c.state == 0) {
+      c.done = take(c, c.xcd);
+      c.state = 1;
+    } else if (c.state == 1) {  // read the counters, pick the fullest pool
+      int32_t best = -(1 << 30);
+      for (int32_t y = 0; y < kXcd; ++y) {
+        int32_t lo, dyn, hi;
+        xcd_range(sp, y, lo, dyn, hi);
+        best = std::max(best, (hi - dyn - cnt[y]) * kXcd + (kXcd - 1 - y));
+      }
+      if (best < kXcd || ++c.rounds > kXcd + 1) c.done = true;
+      else { c.pick = kXcd - 1 - (best & (kXcd - 1)); c.state = 2; }
+    } else {
+      c.done = take(c, c.pick);
+      c.state = 1;
+    }
+    if (c.done) { live[li] = live.back(); live.pop_back(); }
   }
   for (int64_t t = 0; t < ntiles; ++t) expect(seen[t] == 1, "a tile is not taken exactly once", plan);
   // work per XCD: every boundary sits at the first tile whose preceding work
@@ -183,9 +236,11 @@ int main() {
     std::vector<int64_t> r(96, 2048), c(96, 6144);
     Plan pl;
     expect(make_plan(96, r.data(), c.data(), MUON_BF16, pl) == MUON_OK, "uniform plan", -1);
-    expect(pl.split_prod.grid == 18432 && pl.split_gram.grid == 3456, "uniform grid", -1);
+    // 2304 and 432 tiles per XCD; pools of 144 and 32 tiles
+    expect(pl.split_prod.grid == 8 * (2304 + 144) && pl.split_gram.grid == 8 * (432 + 32),
+           "uniform grid", -1);
     for (int x = 0; x <= kXcd; ++x) expect(pl.split_prod.lo[x] == 2304 * x, "uniform ranges", -1);
-    expect(pl.wide_prod && pl.split_prodw.grid == 12288, "uniform wide grid", -1);
+    expect(pl.wide_prod && pl.split_prodw.grid == 8 * (1536 + 96), "uniform wide grid", -1);
     for (int x = 0; x <= kXcd; ++x)
       expect(pl.split_prodw.lo[x] == 1536 * x, "uniform wide ranges", -1);
   }

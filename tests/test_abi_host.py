@@ -58,6 +58,7 @@ def expected_workspace(shapes, esize):
     desc = 112  # sizeof(MatDesc)
     total = up(desc * batch, 256) + up(4 * 7 * (batch + 1), 256)  # 7 phase prefix arrays
     total += up(4 * batch, 256)  # per-matrix 1 / (||U|| + eps)
+    total += up(4 * 2 * 16, 256)  # two sets of 16 tile-claim counters
     # one partial sum of squares per momentum-pass tile of the padded wide
     # iterate: 32 x 256 for a wide matrix (rows <= cols), 256 x 64 for a tall one
     blocks = sum((up(r, 256) // 32) * (up(c, 256) // 256) if r <= c else

@@ -91,13 +91,14 @@ def _up(x, a):
 
 def _workspace_f8(ws, shape, which):
     """The e4m3 buffer `which` (0 or 1) of the only matrix of a one-matrix call,
-    from the workspace layout (muon_internal.hpp): the descriptor table and the
-    7 phase prefix arrays, the inverse norm, the momentum-pass partials, then
-    X ping, X pong, A, B, and the two e4m3 buffers."""
+    from the workspace layout (muon_abi.hip): the descriptor table and the
+    7 phase prefix arrays, the inverse norm, two sets of 16 tile-claim
+    counters, the momentum-pass partials, then X ping, X pong, A, B, and the
+    two e4m3 buffers."""
     r, c = shape
     tall = r > c
     sp, lp = _up(min(shape), 256), _up(max(shape), 256)
-    off = _up(112, 256) + _up(4 * 7 * 2, 256) + _up(4, 256)
+    off = _up(112, 256) + _up(4 * 7 * 2, 256) + _up(4, 256) + _up(4 * 2 * 16, 256)
     blocks = (sp // 256) * (lp // 64) if tall else (sp // 32) * (lp // 256)
     off += _up(4 * blocks, 256)
     off += 2 * _up(sp * lp * 2, 256) + 2 * _up(sp * sp * 2, 256)

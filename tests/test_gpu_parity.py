@@ -649,14 +649,16 @@ def _up(x, a):
 
 def _workspace_sym(ws, shape):
     """A = X X^T and B = c A^2 + b A of the only matrix of a one-matrix bf16 call,
-    read from the workspace (layout in muon_internal.hpp: descriptor table, the 7
-    phase prefix arrays, the inverse norm, the momentum-pass partials, X ping,
-    X pong, A, B; matrices in 256 x 32 slabs) as s_pad x s_pad int16 arrays."""
+    read from the workspace (layout in muon_abi.hip: descriptor table, the 7
+    phase prefix arrays, the inverse norm, two sets of 16 tile-claim counters,
+    the momentum-pass partials, X ping, X pong, A, B; matrices in 256 x 32 slabs)
+    as s_pad x s_pad int16 arrays."""
     r, c = shape
     tall = r > c
     sp, lp = _up(min(shape), 256), _up(max(shape), 256)
     blocks = (sp // 256) * (lp // 64) if tall else (sp // 32) * (lp // 256)
-    off = _up(112, 256) + _up(4 * 7 * 2, 256) + _up(4, 256) + _up(4 * blocks, 256)
+    off = _up(112, 256) + _up(4 * 7 * 2, 256) + _up(4, 256) + _up(4 * 2 * 16, 256)
+    off += _up(4 * blocks, 256)
     off += 2 * _up(sp * lp * 2, 256)
     raw = ws.view(torch.int16)
     out = []
