@@ -84,3 +84,32 @@ def test_noalloc_in_stream_order_and_too_large():
     assert e.value.status == nsa.MUON_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert bool((out == 3.0).all())
+
+
+def test_noalloc_replays_from_a_graph():
+    """The allocation-free call captured into a HIP graph (torch.cuda.CUDAGraph):
+    the capture holds only kernel launches (the descriptor table travels as
+    kernel arguments, the claim counters are zeroed by a kernel, no memset).
+    Three replays, each after eager work that overwrites the outputs and the
+    library's array (an allocation-free call over other matrices), each equal
+    bit for bit to the workspace call's result."""
+    xs = _inputs(FIRST, "bf16", 300)
+    ys = _inputs(SECOND, "bf16", 301)
+    ref = nsa.ns_batched(xs, steps=5)
+    out = [torch.empty_like(x) for x in xs]
+    out_y = [torch.empty_like(y) for y in ys]
+    nsa.ns_batched_noalloc(xs, out, steps=5)  # eager first: the array's address is resolved
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nsa.ns_batched_noalloc(xs, out, steps=5)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in out:
+            o.fill_(5.0)
+        nsa.ns_batched_noalloc(ys, out_y, steps=3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, sh in enumerate(FIRST):
+            assert torch.equal(out[i], ref[i]), (rep, sh)
