@@ -83,7 +83,8 @@ def test_ns_ragged_batch(dtype):
 def test_ns_one_large_among_many_small(dtype):
     """Tiles of very unequal cost in one launch: the XCD ranges, cut by work,
     hold one-tile matrices on either side of a 48-tile one, and the grid has
-    about twice as many workgroups as tiles (the surplus exits at once)."""
+    about twice as many workgroups as tiles (the surplus exits at once, or
+    after finding every pool of run-time tiles empty)."""
     shapes = [(64, 96)] * 20 + [(1536, 2048)] + [(96, 64)] * 20 + [(1024, 300)]
     _ns_check(dtype, shapes)
 
