@@ -20,6 +20,12 @@ with --no-variants).
 measures the plain HBM stream (1 and 2 reads, 1 and 2 writes, 16-byte
 lane-contiguous vectors, with and without the nontemporal hint) that the
 bandwidth-bound kernels are held against.
+
+    python bench.py --tile-timeline [--workload NAME]
+
+reads the per-workgroup timeline of the matrix-core launches from the
+library's timeline build: how busy the CUs were, the idle time between tiles
+and at the end of each launch, and each XCD's share.
 """
 from __future__ import annotations
 
@@ -576,6 +582,93 @@ def bench_overlap(args) -> int:
     return 0 if same else 1
 
 
+TRACE_LIB = os.path.join(ROOT, "newton_schulz_03_amd", "lib", "libmuon_mi355x_tiletrace.so")
+TRACE_SLOTS = ("gram", "a2", "product_wide", "product_square")
+
+
+def bench_tile_timeline(args, wl) -> int:
+    """Per-workgroup timeline of the matrix-core launches of one orthogonalization
+    of the workload's matrices (bf16), from the timeline build of the library
+    (libmuon_mi355x_tiletrace.so: the same kernels plus a start and end stamp on
+    the 100 MHz real-time counter and the hardware ids of the CU, per
+    workgroup).  For the last launch of each kind (Gram, A^2, wide and square
+    product) it reports how busy the CUs were over the launch, the idle time
+    between consecutive tiles on one CU, the idle time at the end, and the
+    tiles and end time of each XCD."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import newton_schulz_03_amd as nsa
+
+    if wl.dtype != "bf16":
+        print("--tile-timeline covers the bf16 kernels", file=sys.stderr)
+        return 1
+    lib = nsa.load_library(TRACE_LIB)
+    if not hasattr(lib, "muon_tile_trace_read"):
+        raise RuntimeError(f"{TRACE_LIB} is not the timeline build")
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(wl.seed)
+    xs = [torch.randn(*sh, generator=gen).to(torch.bfloat16).to(dev) for sh in wl.shapes]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = nsa.allocate_workspace(list(wl.shapes), torch.bfloat16, dev)
+    for _ in range(max(1, args.warmup)):
+        nsa.ns_batched(xs, steps=wl.steps, coeffs=wl.coeffs, out=outs, workspace=ws)
+    torch.cuda.synchronize(dev)
+    if lib.muon_tile_trace_clear() != 0:
+        raise RuntimeError("muon_tile_trace_clear failed")
+    nsa.ns_batched(xs, steps=wl.steps, coeffs=wl.coeffs, out=outs, workspace=ws)
+    torch.cuda.synchronize(dev)
+    nslot, nblk = len(TRACE_SLOTS), 65536
+    buf = np.zeros(nslot * nblk * 3, dtype=np.uint64)
+    lib.muon_tile_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    if lib.muon_tile_trace_read(buf.ctypes.data, buf.nbytes) != 0:
+        raise RuntimeError("muon_tile_trace_read failed")
+    buf = buf.reshape(nslot, nblk, 3)
+    result = {"metric": "matrix-core launch timeline (one orthogonalization, last launch of each kind)",
+              "workload": wl.name, "unit": "us", "launches": {}}
+    for slot, name in enumerate(TRACE_SLOTS):
+        rec = buf[slot]
+        rec = rec[rec[:, 0] > 0]
+        if len(rec) == 0:
+            continue
+        start, end = rec[:, 0].astype(np.int64), rec[:, 1].astype(np.int64)
+        ids = rec[:, 2]
+        tile = (ids & 0xFFFFFF).astype(np.int64) - 1
+        xcd = ((ids >> 24) & 0xF).astype(np.int64)
+        hw = (ids >> 32).astype(np.int64)
+        cu = xcd * 256 + ((hw >> 8) & 0xFF)  # XCD, shader engine, CU
+        work = tile >= 0
+        t0, t1 = start.min(), end.max()
+        span = (t1 - t0) / 100.0
+        busy, gaps, tails, boundaries = [], 0.0, [], 0
+        for k in np.unique(cu[work]):
+            m = work & (cu == k)
+            order = np.argsort(start[m])
+            s_, e_ = start[m][order], end[m][order]
+            busy.append(np.sum(e_ - s_) / 100.0)
+            gaps += np.sum(s_[1:] - e_[:-1]) / 100.0
+            boundaries += len(s_) - 1
+            tails.append((t1 - e_[-1]) / 100.0)
+        dur = (end[work] - start[work]) / 100.0
+        result["launches"][name] = {
+            "workgroups": int(len(rec)), "tiles": int(work.sum()), "cus": int(len(busy)),
+            "truncated": bool(len(rec) >= nblk),  # a larger grid than the timeline holds
+            "span": round(span, 1),
+            "busy_fraction": round(float(np.mean(busy)) / span, 4),
+            "tile_p10_median_p90": [round(float(np.percentile(dur, q)), 1) for q in (10, 50, 90)],
+            "idle_between_tiles_per_cu": round(gaps / len(busy), 1),
+            "idle_per_tile_boundary": round(gaps / max(boundaries, 1), 2),
+            "idle_at_end_mean_max": [round(float(np.mean(tails)), 1), round(float(np.max(tails)), 1)],
+            "xcd_tiles": [int(np.sum(work & (xcd == x))) for x in range(8)],
+            "xcd_last_end": [round(float((end[work & (xcd == x)].max() - t0) / 100.0), 1)
+                             if np.any(work & (xcd == x)) else None for x in range(8)],
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -612,6 +705,9 @@ def main(argv=None) -> int:
                     help="skip the step's e4m3 and host-momentum variants after the headline")
     ap.add_argument("--link-ceiling", action="store_true",
                     help="measure the host link with plain DMA copies of the momentum's size")
+    ap.add_argument("--tile-timeline", action="store_true",
+                    help="per-workgroup timeline of the matrix-core launches, from the library's "
+                         "timeline build")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling hardware traffic counters)")
@@ -631,6 +727,9 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.tile_timeline:  # loads the timeline build instead of the library
+        torch.cuda.set_device(0)
+        return bench_tile_timeline(args, workloads.standard_workloads()[args.workload])
     nsa.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

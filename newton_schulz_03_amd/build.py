@@ -3,7 +3,11 @@
     python -m newton_schulz_03_amd.build [--verbose] [--save-temps DIR]
 
 Every .hip file under csrc/ is compiled to an object (in parallel), then the
-objects are linked into newton_schulz_03_amd/lib/libmuon_mi355x.so.
+objects are linked into newton_schulz_03_amd/lib/libmuon_mi355x.so.  A second
+library, libmuon_mi355x_tiletrace.so, links the same objects except the bf16
+matrix-core source, compiled with -DMUON_TILE_TRACE: its kernels record a
+per-workgroup timeline (`python bench.py --tile-timeline` reads it).  The
+default library's kernels carry none of that code.
 """
 from __future__ import annotations
 
@@ -20,6 +24,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIBNAME = "libmuon_mi355x.so"
+TRACE_LIBNAME = "libmuon_mi355x_tiletrace.so"
+TRACE_SOURCE = "gemm_bf16.hip"  # the one source with timeline hooks
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -42,14 +48,14 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, save_temps: str | None, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, save_temps: str | None, verbose: bool, trace: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + (".trace.o" if trace else ".o"))
+    cmd = [hipcc(), *HIPCC_FLAGS, *(["-DMUON_TILE_TRACE"] if trace else []), "-c", src, "-o", obj]
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
         cmd.insert(1, f"-save-temps={'obj'}")
         obj_dir = save_temps
-        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        obj = os.path.join(obj_dir, os.path.basename(src) + (".trace.o" if trace else ".o"))
         cmd[-1] = obj
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -63,14 +69,8 @@ def _compile(src: str, save_temps: str | None, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, save_temps: str | None = None) -> str:
-    """Compile every kernel source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, save_temps, verbose), srcs))
-    out = os.path.join(LIBDIR, LIBNAME)
+def _link(objs, name: str, verbose: bool) -> str:
+    out = os.path.join(LIBDIR, name)
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
@@ -79,6 +79,22 @@ def build(verbose: bool = False, save_temps: str | None = None) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
     os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, save_temps: str | None = None) -> str:
+    """Compile every kernel source and link the shared library (and the
+    timeline build beside it); returns the library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = sources()
+    jobs = [(s, False) for s in srcs] + [(os.path.join(CSRC, TRACE_SOURCE), True)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], save_temps, verbose, j[1]), jobs))
+    plain, trace_obj = objs[:len(srcs)], objs[-1]
+    out = _link(plain, LIBNAME, verbose)
+    _link([trace_obj if os.path.basename(s) == TRACE_SOURCE else o for s, o in zip(srcs, plain)],
+          TRACE_LIBNAME, verbose)
     return out
 
 

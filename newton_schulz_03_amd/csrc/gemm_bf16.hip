@@ -24,6 +24,47 @@
 
 namespace muon {
 
+// ---------------------------------------------------------------------------
+// Per-workgroup timeline of the bf16 matrix-core launches, for scheduling
+// analysis.  Compiled in only with -DMUON_TILE_TRACE, a separate build of the
+// library (libmuon_mi355x_tiletrace.so); in the default build these functions
+// are empty and the kernels are unchanged.  Each launch kind writes its own
+// slot (0 Gram, 1 A^2, 2 wide product, 3 square product), so the last launch
+// of each kind in a call remains.  Per workgroup: its start and end on the
+// 100 MHz real-time counter, and its tile (or -1) with the hardware ids of
+// the CU it ran on (HW_ID: CU and shader engine; XCC_ID: the XCD).
+constexpr int kTraceSlots = 4;
+constexpr int kTraceBlocks = 65536;
+#ifdef MUON_TILE_TRACE
+__device__ unsigned long long g_tile_trace[kTraceSlots * kTraceBlocks * 3];
+#endif
+
+__device__ __forceinline__ void trace_start(int slot) {
+#ifdef MUON_TILE_TRACE
+  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks)
+    g_tile_trace[(slot * kTraceBlocks + blockIdx.x) * 3] = __builtin_amdgcn_s_memrealtime();
+#else
+  (void)slot;
+#endif
+}
+
+__device__ __forceinline__ void trace_end(int slot, int32_t tile) {
+#ifdef MUON_TILE_TRACE
+  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks) {
+    unsigned long long* r = g_tile_trace + (slot * kTraceBlocks + blockIdx.x) * 3;
+    r[1] = __builtin_amdgcn_s_memrealtime();
+    const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);  // HW_REG_HW_ID, 32 bits
+    const uint32_t xcc_id = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID, 4 bits
+    r[2] = (static_cast<unsigned long long>(hw_id) << 32) |
+           (static_cast<unsigned long long>(xcc_id & 15u) << 24) |
+           (static_cast<uint32_t>(tile + 1) & 0xFFFFFFu);
+  }
+#else
+  (void)slot;
+  (void)tile;
+#endif
+}
+
 namespace {
 
 // Piece u of this thread in the final store: user row (within the tile) and
@@ -866,10 +907,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16(LaunchCtx c, GemmArgs
       __syncthreads();  // every wave is done with LDS before the next tile's loads land there
     }
   } else {
+    constexpr int kSlot = MODE == GM_PROD ? 3 : MODE;
+    trace_start(kSlot);
     __shared__ int claimed;
     const int32_t t = claim_tile(g.split, c, &claimed);
-    if (t < 0) return;  // the whole block
-    gemm_tile<MODE, FINAL, FIRST, false>(c, g, t, smem, &slot);
+    if (t >= 0) gemm_tile<MODE, FINAL, FIRST, false>(c, g, t, smem, &slot);
+    trace_end(kSlot, t);
   }
 }
 
@@ -890,10 +933,11 @@ void launch_one(const LaunchCtx& c, int32_t nblocks, bool loop, const GemmArgs& 
 template <bool FIRST>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_bf16_wide(LaunchCtx c, GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[LDSW];
+  trace_start(2);
   int* slots = reinterpret_cast<int*>(smem + (NST - 1) * STAGEW);  // the lookup's, the claim's
   const int32_t t = claim_tile(g.split, c, slots + 1);
-  if (t < 0) return;  // the whole block
-  gemm_tile_wide<FIRST>(c, g, t, smem, slots);
+  if (t >= 0) gemm_tile_wide<FIRST>(c, g, t, smem, slots);  // the whole block
+  trace_end(2, t);
 }
 
 template <bool FINAL>
@@ -935,3 +979,22 @@ hipError_t launch_prod_wide(const LaunchCtx& c, const XcdSplit& sp, int32_t cur,
 }
 
 }  // namespace muon
+
+#ifdef MUON_TILE_TRACE
+// Copies the timeline (kTraceSlots x kTraceBlocks x 3 uint64) of the current
+// device to host memory; bytes at most its size.  Exported by the timeline
+// build only.  Returns a hipError_t code.
+extern "C" int32_t muon_tile_trace_read(void* host, size_t bytes) {
+  return static_cast<int32_t>(
+      hipMemcpyFromSymbol(host, HIP_SYMBOL(muon::g_tile_trace), bytes, 0, hipMemcpyDeviceToHost));
+}
+
+// Zeroes the timeline of the current device (synchronously).
+extern "C" int32_t muon_tile_trace_clear() {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(muon::g_tile_trace));
+  if (e == hipSuccess) e = hipMemset(p, 0, sizeof(muon::g_tile_trace));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return static_cast<int32_t>(e);
+}
+#endif
