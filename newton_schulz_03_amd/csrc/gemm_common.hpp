@@ -188,23 +188,32 @@ __device__ __forceinline__ void zero_next_sched(const LaunchCtx& c) {
 // depends on blockIdx.x only); lds is one int of LDS.
 //
 // A workgroup past the static part of its XCD's range claims a pool tile.
-// Wave 0 increments its own XCD's counter: the old value k hands out the k-th
-// tile of that pool.  Once that pool is empty, the wave reads all eight
-// counters and claims from the pool with the most tiles left, and repeats
-// while some pool has tiles.
+//
+// Single queue (s.norder > 0): one increment of counter kXcd; the old value k
+// names the k-th entry of the queue, or nothing once k >= s.norder.
+//
+// Per-XCD pools: wave 0 increments its own XCD's counter: the old value k
+// hands out the k-th tile of that pool.  Once that pool is empty, the wave
+// reads all eight counters and claims from the pool with the most tiles left,
+// and repeats while some pool has tiles.
 //
 // Every increment returns a distinct value, so each pool tile goes to exactly
-// one workgroup.  A workgroup gives up only after reading every pool empty.
-// The grid holds at least as many claiming workgroups as pool tiles.  So every
-// tile is taken exactly once.  A failed claim means that pool emptied after it
-// was read, and it is never picked again: at most kXcd failures, so the loop
-// ends.
+// one workgroup.  A workgroup gives up only after finding every pool (or the
+// queue) empty.  The grid holds at least as many claiming workgroups as pool
+// tiles.  So every tile is taken exactly once.  A failed per-XCD claim means
+// that pool emptied after it was read, and it is never picked again: at most
+// kXcd failures, so the loop ends.
 __device__ __forceinline__ int32_t claim_tile(const XcdSplit& s, const LaunchCtx& c, int* lds) {
   const int32_t b = static_cast<int32_t>(blockIdx.x);
   zero_next_sched(c);
   const int32_t t0 = split_tile(s, b);
   if (t0 >= 0 || s.pool == 0) return t0;
-  if (threadIdx.x < 64) {
+  if (s.norder > 0) {
+    if (threadIdx.x == 0) {
+      const int32_t k = atomicAdd(c.sched + kXcd, 1);
+      *lds = k < s.norder ? c.orders[s.order_off + k] : -1;
+    }
+  } else if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int32_t t = -1;
     auto claim = [&](int32_t y) {  // lane 0: one increment of pool y's counter

@@ -76,24 +76,36 @@ struct MatDesc {
 // so that every XCD gets about the same number of K slices to run, not the
 // same number of tiles: in a ragged batch one tile can cost many times another.
 // The last `pool` tiles of each range are not dealt in advance: workgroups
-// claim them while the launch runs (claim_tile), the XCD's own first, so that
-// an XCD that runs faster than the others ends by taking tiles off theirs.
+// claim them while the launch runs (claim_tile), so that an XCD that runs
+// faster than the others ends by taking tiles off theirs.  When the tiles all
+// cost the same, each XCD claims from its own pool first.  When they do not (a
+// ragged batch), the pools form one queue, longest tiles first (`norder`
+// entries of the order table from `order_off`), so that the launch ends with
+// its shortest tiles.
 struct XcdSplit {
   int32_t lo[kXcd + 1];  // XCD x owns tiles [lo[x], lo[x + 1]); lo[kXcd] = all tiles
   int32_t dyn[kXcd];     // its tiles [dyn[x], lo[x + 1]) are claimed at run time
   int32_t pool;          // the most tiles of one range claimed at run time (0: none)
+  int32_t norder;        // > 0: the pools are claimed as one queue of this many tiles
+  int32_t order_off;     // where that queue starts in the order table
   int32_t grid;          // kXcd * (the longest range + pool): the extra workgroups only claim
 };
 
 // Claim counters of the matrix-core launches: kSchedInts int32 per set, two
-// sets used by alternate launches (counter x: tiles claimed from XCD x's pool).
+// sets used by alternate launches (counter x < kXcd: tiles claimed from XCD
+// x's pool; counter kXcd: from the single queue).
 constexpr int kSchedInts = 16;
+// Entries of the order table per matrix-core launch kind (Gram, A^2, product,
+// wide product): a ragged launch whose pools hold more tiles keeps per-XCD pools.
+constexpr int kOrderCap = 2048;
+constexpr int kOrderKinds = 4;
 
 struct LaunchCtx {
   const MatDesc* desc;     // device copy of the descriptors
   const int32_t* prefix;   // device: NPHASE arrays of batch+1 block prefixes
   float* partials;         // device: per prepare-block sums of squares
   float* inv_norm;         // device: per matrix 1 / (||U||_F + eps)
+  const int32_t* orders;   // device: the order table of the single claim queues
   int32_t* sched;          // device: this matrix-core launch's claim counters (zero at its start)
   int32_t* sched_next;     // device: the next one's, which this launch zeroes
   int32_t batch;

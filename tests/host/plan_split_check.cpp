@@ -11,6 +11,8 @@
 //   - a model of the run-time claims (random interleavings of the claiming
 //     workgroups' counter reads and increments) hands out every pool tile
 //     exactly once;
+//   - a ragged launch's single claim queue (not the Gram's) holds exactly its
+//     pool tiles, longest first, and a uniform launch has none;
 //   - every XCD's range holds at most 1/8 of the launch's work plus one tile.
 //   - the tile orders (prod_tile, sym_tile) take every tile of a grid once, and
 //     sym_tile takes the diagonal tiles of each band of kTileGroup rows in a row.
@@ -64,7 +66,8 @@ void expect(bool ok, const char* what, int plan) {
 
 // tiles: per-matrix tile counts; slices: K slices per tile of each matrix
 void check_split(const XcdSplit& sp, const std::vector<int64_t>& tiles,
-                 const std::vector<int64_t>& slices, int plan) {
+                 const std::vector<int64_t>& slices, const std::vector<int32_t>& order, bool queue,
+                 int plan) {
   int64_t ntiles = 0;
   for (int64_t t : tiles) ntiles += t;
   expect(sp.lo[0] == 0 && sp.lo[kXcd] == ntiles, "ranges do not span the tiles", plan);
@@ -89,6 +92,39 @@ void check_split(const XcdSplit& sp, const std::vector<int64_t>& tiles,
     }
     expect(t >= 0 && t < ntiles, "split_tile out of range", plan);
     if (t >= 0 && t < ntiles) seen[t]++;
+  }
+  // a single queue exactly when the pool tiles differ in cost and fit the table
+  std::vector<int64_t> tile_cost;
+  for (size_t i = 0; i < tiles.size(); ++i)
+    for (int64_t k = 0; k < tiles[i]; ++k) tile_cost.push_back(slices[i]);
+  int32_t pooled = 0;
+  int64_t pool_cost = -1;
+  bool ragged = false;
+  for (int x = 0; x < kXcd; ++x)
+    for (int32_t t = sp.dyn[x]; t < sp.lo[x + 1]; ++t) {
+      ++pooled;
+      if (pool_cost < 0) pool_cost = tile_cost[t];
+      ragged = ragged || tile_cost[t] != pool_cost;
+    }
+  expect((sp.norder > 0) == (queue && ragged && pooled <= kOrderCap), "single queue chosen wrongly",
+         plan);
+  if (sp.norder > 0) {
+    // one queue: every pool tile once, costs not increasing; each claimer takes
+    // the next entry (one increment), so entry k goes to the k-th claimer
+    expect(claimers.size() >= static_cast<size_t>(sp.norder), "fewer claimers than queue entries",
+           plan);
+    expect(pooled == sp.norder && sp.norder <= kOrderCap, "queue length", plan);
+    for (int32_t k = 0; k < sp.norder; ++k) {
+      const int32_t t = order[sp.order_off + k];
+      int x = 0;
+      while (x < kXcd && !(t >= sp.dyn[x] && t < sp.lo[x + 1])) ++x;
+      expect(x < kXcd, "queue entry outside the pools", plan);
+      expect(k == 0 || tile_cost[t] <= tile_cost[order[sp.order_off + k - 1]],
+             "queue not longest first", plan);
+      if (t >= 0 && t < ntiles) seen[t]++;
+    }
+    for (int64_t t = 0; t < ntiles; ++t) expect(seen[t] == 1, "a tile is not taken exactly once", plan);
+    return;
   }
   // the run-time claims, modelled step by step in a random interleaving: a
   // claimer increments its own XCD's counter; while it has no tile, it reads
@@ -186,12 +222,12 @@ int main() {
       k_long[i] = pl.desc[i].l_pad / 32;
       k_short[i] = pl.desc[i].s_pad / 32;
     }
-    check_split(pl.split_gram, sym, k_long, trial);
-    check_split(pl.split_poly, sym, k_short, trial);
-    check_split(pl.split_prod, prod, k_short, trial);
+    check_split(pl.split_gram, sym, k_long, pl.order, false, trial);
+    check_split(pl.split_poly, sym, k_short, pl.order, true, trial);
+    check_split(pl.split_prod, prod, k_short, pl.order, true, trial);
     expect(pl.wide_prod == (all_wide && dtype == MUON_BF16), "wide tiles planned wrongly", trial);
     expect(trial < 600 || dtype != MUON_BF16 || pl.wide_prod, "wide-tile batch not wide", trial);
-    if (pl.wide_prod) check_split(pl.split_prodw, prodw, k_short, trial);
+    if (pl.wide_prod) check_split(pl.split_prodw, prodw, k_short, pl.order, true, trial);
     ++plans;
   }
   // the tile orders: every tile of a grid exactly once

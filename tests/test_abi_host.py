@@ -68,6 +68,7 @@ def expected_workspace(shapes, esize):
         s, l = min(r, c), max(r, c)
         sp, lp = up(s, 256), up(l, 256)
         total += 2 * up(sp * lp * esize, 256) + 2 * up(sp * sp * esize, 256)
+    total += up(4 * 4 * 2048, 256)  # last, the claim-queue order table: 4 launch kinds x 2048
     return total
 
 
@@ -270,7 +271,9 @@ def test_workspace_bytes_ex(lib):
     host = nsa.workspace_bytes(shapes, nsa.MUON_BF16, momentum_host=True)
     mbytes = sum(2 * r * c for r, c in shapes)
     biggest = max(2 * r * c for r, c in shapes)
-    assert plain + 2 * mbytes // 16 <= host <= plain + 2 * (mbytes // 16 + biggest) + 16 * 4096
+    # each chunk has its own tables (descriptors, prefixes, the 32 KiB order table)
+    assert plain + 2 * mbytes // 16 <= host <= (plain + 2 * (mbytes // 16 + biggest)
+                                                 + 16 * (4096 + 4 * 4 * 2048))
     both = nsa.workspace_bytes(shapes, nsa.MUON_BF16, fp8=True, momentum_host=True)
     assert both - host == nsa.workspace_bytes(shapes, nsa.MUON_BF16, fp8=True) - plain
     assert lib.muon_workspace_bytes_ex(len(shapes), rows, cols, nsa.MUON_BF16, 4) == ctypes.c_size_t(-1).value
