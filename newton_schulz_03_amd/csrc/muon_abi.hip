@@ -301,9 +301,13 @@ int32_t free_slot(Pool& pool, size_t* idx) {
   return MUON_OK;
 }
 
-// Copies `bytes` composed by `fill` into a pinned slot, then to `dst` on `stream`.
+// Copies `bytes` composed by `fill` into a pinned slot, then to `dst` on
+// `stream`; with bytes2 > 0, the slot's bytes from align_up(bytes, kAlign) on
+// (bytes2 of them, also composed by `fill`) go to dst2 from the same slot.
 template <typename Fill>
-int32_t stage_upload(size_t bytes, Fill fill, void* dst, hipStream_t stream) {
+int32_t stage_upload(size_t bytes, Fill fill, void* dst, hipStream_t stream, size_t bytes2 = 0,
+                     void* dst2 = nullptr) {
+  const size_t host_bytes = bytes2 > 0 ? align_up(bytes, kAlign) + bytes2 : bytes;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -318,20 +322,24 @@ int32_t stage_upload(size_t bytes, Fill fill, void* dst, hipStream_t stream) {
     e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
   }
-  if (s.cap < bytes) {
+  if (s.cap < host_bytes) {
     if (s.host) (void)hipHostFree(s.host);
     s.host = nullptr;
     s.cap = 0;
-    const size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    const size_t cap = std::max<size_t>(host_bytes, 64 * 1024);
     e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc (staging)");
     s.cap = cap;
   }
   char* h = static_cast<char*>(s.host);
-  std::memset(h, 0, bytes);
+  std::memset(h, 0, host_bytes);
   fill(h);
   e = hipMemcpyAsync(dst, h, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (descriptor table)");
+  if (bytes2 > 0) {
+    e = hipMemcpyAsync(dst2, h + align_up(bytes, kAlign), bytes2, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (descriptor table)");
+  }
   e = hipEventRecord(s.done, stream);
   if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   s.pending = true;
@@ -339,20 +347,19 @@ int32_t stage_upload(size_t bytes, Fill fill, void* dst, hipStream_t stream) {
 }
 
 int32_t upload_table(const Plan& pl, void* ws, hipStream_t stream) {
-  int32_t st = stage_upload(
+  // the descriptors and prefixes at the workspace's start; the used part of the
+  // order table, at its end, from the same staging slot
+  const size_t order_bytes = sizeof(int32_t) * pl.order.size();
+  return stage_upload(
       pl.table_bytes,
       [&](char* h) {
         std::memcpy(h, pl.desc.data(), sizeof(MatDesc) * pl.batch);
         std::memcpy(h + align_up(sizeof(MatDesc) * pl.batch, kAlign), pl.prefix.data(),
                     sizeof(int32_t) * pl.prefix.size());
+        if (order_bytes > 0)
+          std::memcpy(h + align_up(pl.table_bytes, kAlign), pl.order.data(), order_bytes);
       },
-      ws, stream);
-  if (st == MUON_OK && !pl.order.empty())
-    st = stage_upload(
-        sizeof(int32_t) * pl.order.size(),
-        [&](char* h) { std::memcpy(h, pl.order.data(), sizeof(int32_t) * pl.order.size()); },
-        static_cast<char*>(ws) + pl.order_off, stream);
-  return st;
+      ws, stream, order_bytes, static_cast<char*>(ws) + pl.order_off);
 }
 
 // The descriptor table as kernel arguments (no staging buffer, nothing but
