@@ -67,22 +67,23 @@ __device__ __forceinline__ void trace_end(int slot, int32_t tile) {
 
 namespace {
 
-// Piece u of this thread in the final store: user row (within the tile) and
-// first of 8 user columns, and the 8 elements of T it carries.  A wide matrix
-// takes rows of T, a tall one columns of T (its rows).
+// Piece u of this thread (tid = 64 wave + lane) in the final store: user row
+// (within the tile) and first of 8 user columns, and the 8 elements of T it
+// carries.  A wide matrix takes rows of T, a tall one columns of T (its rows).
 template <bool TALL>
 struct FinalPiece {
-  static __device__ __forceinline__ int row(int u, int wave, int lane) {
-    return TALL ? 16 * ((32 * wave + u) >> 3) + (lane & 15) : (threadIdx.x >> 5) + 8 * u;
+  static __device__ __forceinline__ int row(int u, int wave, int lane, int tid) {
+    return TALL ? 16 * ((32 * wave + u) >> 3) + (lane & 15) : (tid >> 5) + 8 * u;
   }
-  static __device__ __forceinline__ int col(int u, int wave, int lane) {
-    return TALL ? 8 * (4 * ((32 * wave + u) & 7) + (lane >> 4)) : 8 * (threadIdx.x & 31);
+  static __device__ __forceinline__ int col(int u, int wave, int lane, int tid) {
+    return TALL ? 8 * (4 * ((32 * wave + u) & 7) + (lane >> 4)) : 8 * (tid & 31);
   }
-  static __device__ __forceinline__ u32x4_t tile(const char* smem, int u, int wave, int lane) {
+  static __device__ __forceinline__ u32x4_t tile(const char* smem, int u, int wave, int lane,
+                                                 int tid) {
     if constexpr (TALL) {
       return read_tile_column(smem, 32 * wave + u, lane);
     } else {
-      const int q = (threadIdx.x >> 5) + 8 * u, c = threadIdx.x & 31;
+      const int q = (tid >> 5) + 8 * u, c = tid & 31;
       return *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4));
     }
   }
@@ -94,21 +95,24 @@ struct FinalPiece {
 template <bool TALL>
 __device__ __forceinline__ void store_final_interior(const f32x16_t (&acc)[4][4], float nf,
                                                      uint16_t* base, int64_t cols, bool upd,
-                                                     float step, char* smem, int wave, int lane) {
+                                                     float step, char* smem, int wave, int lane,
+                                                     int tid) {
   using P = FinalPiece<TALL>;
   u32x4_t w[32];
   if (upd) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) w[u] = ld16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane));
+    for (int u = 0; u < 16; ++u)
+      w[u] = ld16(base + P::row(u, wave, lane, tid) * cols + P::col(u, wave, lane, tid));
   }
   stage_tile(acc, nf, smem, wave, lane);
   if (upd) {
 #pragma unroll
-    for (int u = 16; u < 32; ++u) w[u] = ld16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane));
+    for (int u = 16; u < 32; ++u)
+      w[u] = ld16(base + P::row(u, wave, lane, tid) * cols + P::col(u, wave, lane, tid));
   }
 #pragma unroll
   for (int u = 0; u < 32; ++u) {
-    u32x4_t v = P::tile(smem, u, wave, lane);
+    u32x4_t v = P::tile(smem, u, wave, lane, tid);
     if (upd) {
       float x[8], wf[8];
       vec_to_f32<uint16_t>(v, x);
@@ -117,7 +121,7 @@ __device__ __forceinline__ void store_final_interior(const f32x16_t (&acc)[4][4]
       for (int e = 0; e < 8; ++e) x[e] = wf[e] - step * x[e];
       v = f32_to_vec<uint16_t>(x);
     }
-    st16(base + P::row(u, wave, lane) * cols + P::col(u, wave, lane), v);
+    st16(base + P::row(u, wave, lane, tid) * cols + P::col(u, wave, lane, tid), v);
   }
 }
 
@@ -127,15 +131,15 @@ template <bool TALL>
 __device__ __forceinline__ void store_final_edge(const f32x16_t (&acc)[4][4], float nf,
                                                  const MatDesc& d, int64_t ur0, int64_t uc0,
                                                  bool upd, float step, char* smem, int wave,
-                                                 int lane) {
+                                                 int lane, int tid) {
   using P = FinalPiece<TALL>;
   uint16_t* __restrict__ out = static_cast<uint16_t*>(d.dst);
   const int64_t rows = d.rows, cols = d.cols;
   stage_tile(acc, nf, smem, wave, lane);
 #pragma unroll 1
   for (int u = 0; u < 32; ++u) {
-    const int64_t r = ur0 + P::row(u, wave, lane), c = uc0 + P::col(u, wave, lane);
-    const u32x4_t xv = P::tile(smem, u, wave, lane);
+    const int64_t r = ur0 + P::row(u, wave, lane, tid), c = uc0 + P::col(u, wave, lane, tid);
+    const u32x4_t xv = P::tile(smem, u, wave, lane, tid);
     if (r >= rows || c >= cols) continue;
     float x[8];
     vec_to_f32<uint16_t>(xv, x);
@@ -162,7 +166,7 @@ __device__ __forceinline__ void store_final_edge(const f32x16_t (&acc)[4][4], fl
 // staged in LDS as for the iterate.
 __device__ __forceinline__ void store_final(const f32x16_t (&acc)[4][4], const TileRef& tr,
                                             const GemmArgs& g, float nf, char* smem, int wave,
-                                            int lane) {
+                                            int lane, int tid) {
   const MatDesc& d = tr.d;
   const bool tall = d.tall != 0;
   const bool upd = g.finish == FIN_STEP;
@@ -173,14 +177,14 @@ __device__ __forceinline__ void store_final(const f32x16_t (&acc)[4][4], const T
   uint16_t* base = static_cast<uint16_t*>(d.dst) + ur0 * d.cols + uc0;
   if (interior) {
     if (tall)
-      store_final_interior<true>(acc, nf, base, d.cols, upd, step, smem, wave, lane);
+      store_final_interior<true>(acc, nf, base, d.cols, upd, step, smem, wave, lane, tid);
     else
-      store_final_interior<false>(acc, nf, base, d.cols, upd, step, smem, wave, lane);
+      store_final_interior<false>(acc, nf, base, d.cols, upd, step, smem, wave, lane, tid);
   } else {
     if (tall)
-      store_final_edge<true>(acc, nf, d, ur0, uc0, upd, step, smem, wave, lane);
+      store_final_edge<true>(acc, nf, d, ur0, uc0, upd, step, smem, wave, lane, tid);
     else
-      store_final_edge<false>(acc, nf, d, ur0, uc0, upd, step, smem, wave, lane);
+      store_final_edge<false>(acc, nf, d, ur0, uc0, upd, step, smem, wave, lane, tid);
   }
 }
 
@@ -338,10 +342,11 @@ __device__ __forceinline__ void diag_wave(const LaunchCtx& c, const GemmArgs& g,
 // S[ti*256 + q][ti*256 + p] (on and below the diagonal), columns of T where
 // p's block < q's block to S[ti*256 + p][ti*256 + q] (above it).
 template <int MODE>
-__device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wave, int lane) {
+__device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wave, int lane,
+                                           int tid) {
   uint16_t* dst = static_cast<uint16_t*>(MODE == GM_GRAM ? tr.d.gram : tr.d.poly);
   const int64_t ld = tr.d.s_pad, o = static_cast<int64_t>(tr.ti) * kTile;
-  const int t = threadIdx.x, ch = t & 31;
+  const int t = tid, ch = t & 31;
 #pragma unroll 8
   for (int u = 0; u < 32; ++u) {
     const int q = (t >> 5) + 8 * u;
@@ -362,7 +367,7 @@ __device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wa
 
 template <int MODE>
 __device__ __forceinline__ void diag_tile(const LaunchCtx& c, const GemmArgs& g, const TileRef& tr,
-                                          char* smem, int lane) {
+                                          char* smem, int lane, int tid) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   switch (wave) {
     case 0: diag_wave<MODE, 0>(c, g, tr, smem, lane); break;
@@ -371,7 +376,7 @@ __device__ __forceinline__ void diag_tile(const LaunchCtx& c, const GemmArgs& g,
     default: diag_wave<MODE, 3>(c, g, tr, smem, lane); break;
   }
   __syncthreads();
-  diag_store<MODE>(tr, smem, wave, lane);
+  diag_store<MODE>(tr, smem, wave, lane, tid);
 }
 
 // One output tile (tile number t of the launch).  FINAL (products only): the last product
@@ -388,16 +393,20 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   // LOOP: the lane index passes through an empty asm, so that the per-lane
   // offsets and identity fragments derived from it are formed anew for every
   // tile instead of being hoisted out of the tile loop and held live through
-  // the epilogue (which made the looping kernels spill more).
+  // the epilogue (which made the looping kernels spill more).  The epilogues
+  // take the thread index as tid, formed from that lane, for the same reason:
+  // their per-thread store addresses, from threadIdx.x itself, were hoisted and
+  // spilled (67 values stored before the tile loop, 98 reloads per tile).
   int lane = threadIdx.x & 63;
   if constexpr (LOOP) asm volatile("" : "+v"(lane));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = LOOP ? 64 * wave + lane : static_cast<int>(threadIdx.x);
   if constexpr (MODE != GM_PROD) {
     if (tr.ti == tr.tj) {
-      diag_tile<MODE>(c, g, tr, smem, lane);
+      diag_tile<MODE>(c, g, tr, smem, lane, tid);
       return;
     }
   }
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
 
@@ -599,9 +608,9 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   // every other product stages with an exact 1 (no multiply)
   const float nf = MODE == GM_PROD ? (FIRST ? c.inv_norm[tr.mat] : 1.f) : norm_factor<MODE>(c, g, tr);
   if constexpr (FINAL)
-    store_final(acc, tr, g, nf, smem, wave, lane);
+    store_final(acc, tr, g, nf, smem, wave, lane, tid);
   else
-    store_tile_lds<MODE>(acc, tr, g, nf, smem, wave, lane);
+    store_tile_lds<MODE>(acc, tr, g, nf, smem, wave, lane, tid);
 }
 
 // ---------------------------------------------------------------------------

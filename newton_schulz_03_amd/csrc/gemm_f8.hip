@@ -242,7 +242,7 @@ __device__ __forceinline__ void gemm_tile_f8(const LaunchCtx& c, const GemmArgs&
   __syncthreads();
   if constexpr (MODE != GM_GRAM) add_term<MODE>(acc, tr, g);
   const float nf = MODE == GM_PROD ? (FIRST ? c.inv_norm[tr.mat] : 1.f) : norm_factor<MODE>(c, g, tr);
-  store_tile_lds<MODE>(acc, tr, g, nf, smem, wave, lane);
+  store_tile_lds<MODE>(acc, tr, g, nf, smem, wave, lane, static_cast<int>(threadIdx.x));
 }
 
 }  // namespace

@@ -214,9 +214,9 @@ __device__ __forceinline__ u32x4_t read_tile_column(const char* smem, int I, int
 template <int MODE>
 __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], const TileRef& tr,
                                                const GemmArgs& g, float nf, char* smem, int wave,
-                                               int lane) {
+                                               int lane, int tid) {
   stage_tile(acc, MODE == GM_PROD ? nf : g.out_scale * nf, smem, wave, lane);
-  const int t = threadIdx.x;
+  const int t = tid;  // threadIdx.x
   // Rows of T: thread t moves chunk (t & 31) of rows (t >> 5) + 8u.
   {
     uint16_t* dst;
