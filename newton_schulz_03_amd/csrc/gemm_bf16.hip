@@ -352,7 +352,7 @@ __device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wa
     const int q = (t >> 5) + 8 * u;
     if ((ch >> 2) <= (q >> 5)) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((ch ^ (q & 31)) << 4));
-      st16(dst + slab_off(o + q, o + 8 * ch, ld), v);
+      st16_nt(dst + slab_off(o + q, o + 8 * ch, ld), v);  // as in store_tile_lds
     }
   }
   const int grp = lane >> 4, j = lane & 15;
@@ -361,7 +361,7 @@ __device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wa
     const int I = 32 * wave + u;
     const int pb = I >> 3, cq = 4 * (I & 7) + grp;
     if ((pb >> 1) < (cq >> 2))
-      st16(dst + slab_off(o + 16 * pb + j, o + 8 * cq, ld), read_tile_column(smem, I, lane));
+      st16_nt(dst + slab_off(o + 16 * pb + j, o + 8 * cq, ld), read_tile_column(smem, I, lane));
   }
 }
 

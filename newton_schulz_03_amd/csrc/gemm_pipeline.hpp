@@ -237,7 +237,12 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
     for (int u = 0; u < 32; ++u) {
       const int q = (t >> 5) + 8 * u;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4));
-      st16(dst + slab_off(r0 + q, c0 + 8 * c, ld), v);
+      // A and B go out with the nontemporal hint (measured: Gram and A^2
+      // launches and the call 0.4% faster); the iterate without it (+0.8%)
+      if constexpr (MODE == GM_PROD)
+        st16(dst + slab_off(r0 + q, c0 + 8 * c, ld), v);
+      else
+        st16_nt(dst + slab_off(r0 + q, c0 + 8 * c, ld), v);
     }
   }
   if constexpr (MODE != GM_PROD) {
@@ -254,7 +259,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
       for (int u = 0; u < 32; ++u) {
         const int I = 32 * wave + u;
         const int pb = I >> 3, cq = 4 * (I & 7) + grp;
-        st16(dst + slab_off(r0 + 16 * pb + j, c0 + 8 * cq, ld), read_tile_column(smem, I, lane));
+        st16_nt(dst + slab_off(r0 + 16 * pb + j, c0 + 8 * cq, ld), read_tile_column(smem, I, lane));
       }
     }
   }
