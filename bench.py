@@ -593,8 +593,10 @@ def bench_tile_timeline(args, wl) -> int:
     the 100 MHz real-time counter and the hardware ids of the CU, per
     workgroup).  For the last launch of each kind (Gram, A^2, wide and square
     product) it reports how busy the CUs were over the launch, the idle time
-    between consecutive tiles on one CU, the idle time at the end, and the
-    tiles and end time of each XCD."""
+    between consecutive tiles on one CU, the idle time at the end, the tiles
+    and end time of each XCD, and how an off-diagonal tile's time splits into
+    claim and prologue (until the first slice is in LDS), K loop and epilogue
+    (from the last slice to the stores issued)."""
     import ctypes
 
     import numpy as np
@@ -620,12 +622,14 @@ def bench_tile_timeline(args, wl) -> int:
         raise RuntimeError("muon_tile_trace_clear failed")
     nsa.ns_batched(xs, steps=wl.steps, coeffs=wl.coeffs, out=outs, workspace=ws)
     torch.cuda.synchronize(dev)
-    nslot, nblk = len(TRACE_SLOTS), 65536
-    buf = np.zeros(nslot * nblk * 3, dtype=np.uint64)
+    nslot, nblk, nword = len(TRACE_SLOTS), 65536, 5
+    buf = np.zeros(nslot * nblk * nword, dtype=np.uint64)
     lib.muon_tile_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     if lib.muon_tile_trace_read(buf.ctypes.data, buf.nbytes) != 0:
         raise RuntimeError("muon_tile_trace_read failed")
-    buf = buf.reshape(nslot, nblk, 3)
+    buf = buf.reshape(nslot, nblk, nword)
+    if args.timeline_raw:
+        np.save(args.timeline_raw, buf)
     result = {"metric": "matrix-core launch timeline (one orthogonalization, last launch of each kind)",
               "workload": wl.name, "unit": "us", "launches": {}}
     for slot, name in enumerate(TRACE_SLOTS):
@@ -652,6 +656,14 @@ def bench_tile_timeline(args, wl) -> int:
             boundaries += len(s_) - 1
             tails.append((t1 - e_[-1]) / 100.0)
         dur = (end[work] - start[work]) / 100.0
+        # off-diagonal tiles: start -> K loop -> epilogue (claim and prologue, K loop, epilogue)
+        kb, ke = rec[:, 3].astype(np.int64), rec[:, 4].astype(np.int64)
+        ph = work & (kb > 0) & (ke >= kb)
+        phases = None
+        if np.any(ph):
+            phases = {k: [round(float(np.percentile(v, q)), 2) for q in (10, 50, 90)] for k, v in (
+                ("prologue", (kb[ph] - start[ph]) / 100.0), ("k_loop", (ke[ph] - kb[ph]) / 100.0),
+                ("epilogue", (end[ph] - ke[ph]) / 100.0))}
         result["launches"][name] = {
             "workgroups": int(len(rec)), "tiles": int(work.sum()), "cus": int(len(busy)),
             "truncated": bool(len(rec) >= nblk),  # a larger grid than the timeline holds
@@ -661,6 +673,7 @@ def bench_tile_timeline(args, wl) -> int:
             "idle_between_tiles_per_cu": round(gaps / len(busy), 1),
             "idle_per_tile_boundary": round(gaps / max(boundaries, 1), 2),
             "idle_at_end_mean_max": [round(float(np.mean(tails)), 1), round(float(np.max(tails)), 1)],
+            "phases_p10_median_p90": phases,
             "xcd_tiles": [int(np.sum(work & (xcd == x))) for x in range(8)],
             "xcd_last_end": [round(float((end[work & (xcd == x)].max() - t0) / 100.0), 1)
                              if np.any(work & (xcd == x)) else None for x in range(8)],
@@ -708,6 +721,9 @@ def main(argv=None) -> int:
     ap.add_argument("--tile-timeline", action="store_true",
                     help="per-workgroup timeline of the matrix-core launches, from the library's "
                          "timeline build")
+    ap.add_argument("--timeline-raw", default="",
+                    help="with --tile-timeline: also save the raw per-workgroup records (numpy, "
+                         "slots x workgroups x [start, end, ids, K loop start, K loop end])")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling hardware traffic counters)")

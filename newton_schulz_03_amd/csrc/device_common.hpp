@@ -31,6 +31,14 @@ template <> struct Elt<uint16_t> {
   static __device__ __forceinline__ uint16_t from_f32(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
   }
+  // from_f32(lo) | from_f32(hi) << 16 in one packed conversion (the same
+  // rounding; written element by element it took four instructions).
+  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+  }
 };
 
 template <> struct Elt<float> {
@@ -60,9 +68,7 @@ __device__ __forceinline__ u32x4_t f32_to_vec(const float* in) {
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint32_t lo = Elt<uint16_t>::from_f32(in[2 * i]);
-      uint32_t hi = Elt<uint16_t>::from_f32(in[2 * i + 1]);
-      v[i] = lo | (hi << 16);
+      v[i] = Elt<uint16_t>::pack2(in[2 * i], in[2 * i + 1]);
     }
   } else {
 #pragma unroll
@@ -182,6 +188,16 @@ constexpr int kSlabCols = 32;
 __device__ __forceinline__ int64_t slab_off(int64_t r, int64_t c, int64_t ncols) {
   return ((r / kSlabRows) * (ncols / kSlabCols) + c / kSlabCols) * (kSlabRows * kSlabCols) +
          (r % kSlabRows) * kSlabCols + (c % kSlabCols);
+}
+// Offset of (r0 + q, c0 + cc) from (r0, c0), for r0 a multiple of kSlabRows,
+// c0 a multiple of kSlabCols, 0 <= q < kSlabRows and cc >= 0: the same band,
+// slab cc / kSlabCols after c0's.  Unsigned 32-bit shifts and masks only.  The
+// matrix-core epilogues add it to their tile's origin, slab_off(r0, c0, ncols),
+// which is uniform over the workgroup; computing slab_off per store (signed
+// 64-bit division and products) cost about 40 VALU instructions per 16-byte
+// store and most of the epilogue's time.
+__device__ __forceinline__ uint32_t slab_local(uint32_t q, uint32_t cc) {
+  return (cc / kSlabCols) * (kSlabRows * kSlabCols) + q * kSlabCols + (cc % kSlabCols);
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs of the chip (block b runs on

@@ -30,28 +30,44 @@ namespace muon {
 // library (libmuon_mi355x_tiletrace.so); in the default build these functions
 // are empty and the kernels are unchanged.  Each launch kind writes its own
 // slot (0 Gram, 1 A^2, 2 wide product, 3 square product), so the last launch
-// of each kind in a call remains.  Per workgroup: its start and end on the
-// 100 MHz real-time counter, and its tile (or -1) with the hardware ids of
-// the CU it ran on (HW_ID: CU and shader engine; XCC_ID: the XCD).
-constexpr int kTraceSlots = 4;
-constexpr int kTraceBlocks = 65536;
+// of each kind in a call remains.  Per workgroup (kTraceWords values): its
+// start and end on the 100 MHz real-time counter, its tile (or -1) with the
+// hardware ids of the CU it ran on (HW_ID: CU and shader engine; XCC_ID: the
+// XCD), and, for off-diagonal tiles, the moments its K loop began (first
+// slice in LDS, after the barrier) and ended (last MFMA issued and every load
+// landed, after the barrier): prologue, K loop and epilogue of each tile.
+[[maybe_unused]] constexpr int kTraceSlots = 4;
+[[maybe_unused]] constexpr int kTraceBlocks = 65536;
+[[maybe_unused]] constexpr int kTraceWords = 5;  // start, end, ids, K loop start, K loop end
 #ifdef MUON_TILE_TRACE
-__device__ unsigned long long g_tile_trace[kTraceSlots * kTraceBlocks * 3];
+__device__ unsigned long long g_tile_trace[kTraceSlots * kTraceBlocks * kTraceWords];
 #endif
 
 __device__ __forceinline__ void trace_start(int slot) {
 #ifdef MUON_TILE_TRACE
   if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks)
-    g_tile_trace[(slot * kTraceBlocks + blockIdx.x) * 3] = __builtin_amdgcn_s_memrealtime();
+    g_tile_trace[(slot * kTraceBlocks + blockIdx.x) * kTraceWords] = __builtin_amdgcn_s_memrealtime();
 #else
   (void)slot;
+#endif
+}
+
+// word 3: the K loop begins, word 4: it has ended (single-tile kernels only)
+__device__ __forceinline__ void trace_phase(int slot, int word) {
+#ifdef MUON_TILE_TRACE
+  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks)
+    g_tile_trace[(slot * kTraceBlocks + blockIdx.x) * kTraceWords + word] =
+        __builtin_amdgcn_s_memrealtime();
+#else
+  (void)slot;
+  (void)word;
 #endif
 }
 
 __device__ __forceinline__ void trace_end(int slot, int32_t tile) {
 #ifdef MUON_TILE_TRACE
   if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks) {
-    unsigned long long* r = g_tile_trace + (slot * kTraceBlocks + blockIdx.x) * 3;
+    unsigned long long* r = g_tile_trace + (slot * kTraceBlocks + blockIdx.x) * kTraceWords;
     r[1] = __builtin_amdgcn_s_memrealtime();
     const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);  // HW_REG_HW_ID, 32 bits
     const uint32_t xcc_id = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID, 4 bits
@@ -329,10 +345,8 @@ __device__ __forceinline__ void diag_wave(const LaunchCtx& c, const GemmArgs& g,
     for (int gg = 0; gg < 4; ++gg) {
       const int ch = 4 * DW::row(i) + gg;
       u32x2_t w;
-      w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 0])) |
-             (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 1])) << 16);
-      w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 2])) |
-             (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[i][4 * gg + 3])) << 16);
+      w[0] = Elt<uint16_t>::pack2(scale * acc[i][4 * gg + 0], scale * acc[i][4 * gg + 1]);
+      w[1] = Elt<uint16_t>::pack2(scale * acc[i][4 * gg + 2], scale * acc[i][4 * gg + 3]);
       *reinterpret_cast<u32x2_t*>(smem + q * MNROW + ((ch ^ (q & 31)) << 4) + 8 * lh) = w;
     }
   });
@@ -346,13 +360,14 @@ __device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wa
                                            int tid) {
   uint16_t* dst = static_cast<uint16_t*>(MODE == GM_GRAM ? tr.d.gram : tr.d.poly);
   const int64_t ld = tr.d.s_pad, o = static_cast<int64_t>(tr.ti) * kTile;
+  uint16_t* const org = dst + slab_off(o, o, ld);  // the tile's origin (uniform)
   const int t = tid, ch = t & 31;
 #pragma unroll 8
   for (int u = 0; u < 32; ++u) {
     const int q = (t >> 5) + 8 * u;
     if ((ch >> 2) <= (q >> 5)) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + q * MNROW + ((ch ^ (q & 31)) << 4));
-      st16_nt(dst + slab_off(o + q, o + 8 * ch, ld), v);  // as in store_tile_lds
+      st16_nt(org + slab_local(q, 8 * ch), v);  // as in store_tile_lds
     }
   }
   const int grp = lane >> 4, j = lane & 15;
@@ -361,7 +376,7 @@ __device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wa
     const int I = 32 * wave + u;
     const int pb = I >> 3, cq = 4 * (I & 7) + grp;
     if ((pb >> 1) < (cq >> 2))
-      st16_nt(dst + slab_off(o + 16 * pb + j, o + 8 * cq, ld), read_tile_column(smem, I, lane));
+      st16_nt(org + slab_local(16 * pb + j, 8 * cq), read_tile_column(smem, I, lane));
   }
 }
 
@@ -540,6 +555,7 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   }
   wait_vm<(NST - 2) * 2 * LPO>();
   __syncthreads();
+  if constexpr (!LOOP) trace_phase(MODE == GM_PROD ? 3 : MODE, 3);
 
   Frags f0, f1;
 #pragma unroll
@@ -604,6 +620,7 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   }
   wait_vm<0>();  // no load may still target LDS: the ring is reused for the store
   __syncthreads();
+  if constexpr (!LOOP) trace_phase(MODE == GM_PROD ? 3 : MODE, 4);
   // the norm factor: a product takes it only in its FIRST instantiation, so
   // every other product stages with an exact 1 (no multiply)
   const float nf = MODE == GM_PROD ? (FIRST ? c.inv_norm[tr.mat] : 1.f) : norm_factor<MODE>(c, g, tr);
@@ -681,6 +698,7 @@ __device__ __forceinline__ void store_wide(const f32x16_t (&acc)[4][4], const f3
   const int64_t ld = tr.d.l_pad;
   const int64_t r0 = static_cast<int64_t>(tr.ti) * kTile;
   const int64_t cw = static_cast<int64_t>(tr.tj) * kTileW;
+  uint16_t* const org = dst + slab_off(r0, cw, ld);  // the tile's origin (uniform)
   // p-block 3h + ml of this wave (its four q-blocks) into the staged half
   auto stage_mi = [&](const f32x16_t (&a)[4], int ml) {
 #pragma unroll
@@ -690,24 +708,28 @@ __device__ __forceinline__ void store_wide(const f32x16_t (&acc)[4][4], const f3
         const int q = wn * 128 + ni * 32 + lr;
         const int c = 12 * wm + 4 * ml + gg;
         u32x2_t w;
-        w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 0])) |
-               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 1])) << 16);
-        w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 2])) |
-               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(nf * a[ni][4 * gg + 3])) << 16);
+        w[0] = Elt<uint16_t>::pack2(nf * a[ni][4 * gg + 0], nf * a[ni][4 * gg + 1]);
+        w[1] = Elt<uint16_t>::pack2(nf * a[ni][4 * gg + 2], nf * a[ni][4 * gg + 3]);
         *reinterpret_cast<u32x2_t*>(smem + q * WROW + ((c ^ ((q >> 1) & 7)) << 4) + 8 * lh) = w;
       }
   };
   auto store_half = [&](int h) {
-#pragma unroll 4
-    for (int v = 0; v < 24; ++v) {
-      const int unit = 24 * wave + v;  // slab gs = unit % 6 of the half, rows 16 (unit / 6) ..
-      const int gs = unit % 6, rg = unit / 6;
-      const int q = 16 * rg + (lane & 15);
-      const int c = 4 * gs + (lane >> 4);
-      const u32x4_t val =
-          *reinterpret_cast<const u32x4_t*>(smem + q * WROW + ((c ^ ((q >> 1) & 7)) << 4));
-      const int64_t col = cw + 192 * (gs / 3) + 96 * h + 32 * (gs % 3) + 8 * (lane >> 4);
-      st16(dst + slab_off(r0 + q, col, ld), val);
+#pragma unroll 1
+    for (int k = 0; k < 4; ++k) {
+      // units 24 wave + 6 k + gs: slab gs of the half, rows 16 (4 wave + k) ..; the
+      // six LDS reads go out before the six stores, so that their latencies overlap
+      const int q = 16 * (4 * wave + k) + (lane & 15);
+      u32x4_t val[6];
+#pragma unroll
+      for (int gs = 0; gs < 6; ++gs) {
+        const int c = 4 * gs + (lane >> 4);
+        val[gs] = *reinterpret_cast<const u32x4_t*>(smem + q * WROW + ((c ^ ((q >> 1) & 7)) << 4));
+      }
+#pragma unroll
+      for (int gs = 0; gs < 6; ++gs) {
+        const int col = 192 * (gs / 3) + 96 * h + 32 * (gs % 3) + 8 * (lane >> 4);  // in the tile
+        st16(org + slab_local(q, col), val[gs]);
+      }
     }
   };
   stage_mi(acc[0], 0);
@@ -842,6 +864,7 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
   }
   wait_vm<(NST - 2) * (LPW + LPO)>();
   __syncthreads();
+  trace_phase(2, 3);
 
   FragsW f0, f1;
 #pragma unroll
@@ -894,6 +917,7 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
   for (int kt = rel0 + 4; kt < nk; ++kt) slice(kt, NoTerm{});
   wait_vm<0>();
   __syncthreads();
+  trace_phase(2, 4);
   mfma_guard(accv);
   const float nf = FIRST ? c.inv_norm[tr.mat] : 1.f;
   store_wide(acc, accv, tr, g, nf, smem, wave, lane);
@@ -990,7 +1014,7 @@ hipError_t launch_prod_wide(const LaunchCtx& c, const XcdSplit& sp, int32_t cur,
 }  // namespace muon
 
 #ifdef MUON_TILE_TRACE
-// Copies the timeline (kTraceSlots x kTraceBlocks x 3 uint64) of the current
+// Copies the timeline (kTraceSlots x kTraceBlocks x kTraceWords uint64) of the current
 // device to host memory; bytes at most its size.  Exported by the timeline
 // build only.  Returns a hipError_t code.
 extern "C" int32_t muon_tile_trace_read(void* host, size_t bytes) {

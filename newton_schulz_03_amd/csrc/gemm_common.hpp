@@ -61,10 +61,8 @@ template <typename T>
 __device__ __forceinline__ void store4(T* p, const float* v) {
   if constexpr (sizeof(T) == 2) {
     u32x2_t w;
-    w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[0])) |
-           (static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[1])) << 16);
-    w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[2])) |
-           (static_cast<uint32_t>(Elt<uint16_t>::from_f32(v[3])) << 16);
+    w[0] = Elt<uint16_t>::pack2(v[0], v[1]);
+    w[1] = Elt<uint16_t>::pack2(v[2], v[3]);
     *reinterpret_cast<u32x2_t*>(p) = w;
   } else {
     u32x4_t w;

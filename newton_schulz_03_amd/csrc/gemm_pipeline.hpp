@@ -183,10 +183,8 @@ __device__ __forceinline__ void stage_tile(const f32x16_t (&acc)[4][4], float sc
         const int q = wn * 128 + ni * 32 + lr;
         const int c = 16 * wm + 4 * mi + gg;  // chunk of p0 = wm*128 + mi*32 + 8gg (+4lh)
         u32x2_t w;
-        w[0] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 0])) |
-               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 1])) << 16);
-        w[1] = static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 2])) |
-               (static_cast<uint32_t>(Elt<uint16_t>::from_f32(scale * acc[mi][ni][4 * gg + 3])) << 16);
+        w[0] = Elt<uint16_t>::pack2(scale * acc[mi][ni][4 * gg + 0], scale * acc[mi][ni][4 * gg + 1]);
+        w[1] = Elt<uint16_t>::pack2(scale * acc[mi][ni][4 * gg + 2], scale * acc[mi][ni][4 * gg + 3]);
         *reinterpret_cast<u32x2_t*>(smem + q * MNROW + ((c ^ (q & 31)) << 4) + 8 * lh) = w;
       }
   __syncthreads();
@@ -232,6 +230,7 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
       r0 = static_cast<int64_t>(tr.tj) * kTile;
       c0 = static_cast<int64_t>(tr.ti) * kTile;
     }
+    uint16_t* const org = dst + slab_off(r0, c0, ld);  // the tile's origin (uniform)
     const int c = t & 31;
 #pragma unroll 8
     for (int u = 0; u < 32; ++u) {
@@ -240,9 +239,9 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
       // A and B go out with the nontemporal hint (measured: Gram and A^2
       // launches and the call 0.4% faster); the iterate without it (+0.8%)
       if constexpr (MODE == GM_PROD)
-        st16(dst + slab_off(r0 + q, c0 + 8 * c, ld), v);
+        st16(org + slab_local(q, 8 * c), v);
       else
-        st16_nt(dst + slab_off(r0 + q, c0 + 8 * c, ld), v);
+        st16_nt(org + slab_local(q, 8 * c), v);
     }
   }
   if constexpr (MODE != GM_PROD) {
@@ -254,12 +253,13 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
       const int64_t ld = tr.d.s_pad;
       const int64_t r0 = static_cast<int64_t>(tr.ti) * kTile;
       const int64_t c0 = static_cast<int64_t>(tr.tj) * kTile;
+      uint16_t* const org = dst + slab_off(r0, c0, ld);
       const int grp = lane >> 4, j = lane & 15;
 #pragma unroll 4
       for (int u = 0; u < 32; ++u) {
         const int I = 32 * wave + u;
         const int pb = I >> 3, cq = 4 * (I & 7) + grp;
-        st16_nt(dst + slab_off(r0 + 16 * pb + j, c0 + 8 * cq, ld), read_tile_column(smem, I, lane));
+        st16_nt(org + slab_local(16 * pb + j, 8 * cq), read_tile_column(smem, I, lane));
       }
     }
   }
