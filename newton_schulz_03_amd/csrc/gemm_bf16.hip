@@ -371,12 +371,15 @@ __device__ __forceinline__ void diag_store(const TileRef& tr, char* smem, int wa
     }
   }
   const int grp = lane >> 4, j = lane & 15;
-#pragma unroll 4
-  for (int u = 0; u < 32; ++u) {
-    const int I = 32 * wave + u;
-    const int pb = I >> 3, cq = 4 * (I & 7) + grp;
-    if ((pb >> 1) < (cq >> 2))
-      st16_nt(org + slab_local(16 * pb + j, 8 * cq), read_tile_column(smem, I, lane));
+#pragma unroll 1
+  for (int ub = 0; ub < 4; ++ub) {  // I & 7 = m constant, as in store_tile_lds
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int I = 32 * wave + 8 * ub + m;
+      const int pb = I >> 3, cq = 4 * (I & 7) + grp;
+      if ((pb >> 1) < (cq >> 2))
+        st16_nt(org + slab_local(16 * pb + j, 8 * cq), read_tile_column(smem, I, lane));
+    }
   }
 }
 

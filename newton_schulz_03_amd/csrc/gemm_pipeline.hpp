@@ -255,11 +255,17 @@ __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[4][4], cons
       const int64_t c0 = static_cast<int64_t>(tr.tj) * kTile;
       uint16_t* const org = dst + slab_off(r0, c0, ld);
       const int grp = lane >> 4, j = lane & 15;
-#pragma unroll 4
-      for (int u = 0; u < 32; ++u) {
-        const int I = 32 * wave + u;
-        const int pb = I >> 3, cq = 4 * (I & 7) + grp;
-        st16_nt(org + slab_local(16 * pb + j, 8 * cq), read_tile_column(smem, I, lane));
+      // I = 32 wave + 8 ub + m: I & 7 = m is a constant of the unrolled inner
+      // loop, so the LDS and global offsets that depend on it fold into
+      // immediates (with a runtime u, the swizzle was recomputed per store).
+#pragma unroll 1
+      for (int ub = 0; ub < 4; ++ub) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int I = 32 * wave + 8 * ub + m;
+          const int pb = I >> 3, cq = 4 * (I & 7) + grp;
+          st16_nt(org + slab_local(16 * pb + j, 8 * cq), read_tile_column(smem, I, lane));
+        }
       }
     }
   }
