@@ -595,8 +595,9 @@ def bench_tile_timeline(args, wl) -> int:
     product) it reports how busy the CUs were over the launch, the idle time
     between consecutive tiles on one CU, the idle time at the end, the tiles
     and end time of each XCD, and how an off-diagonal tile's time splits into
-    claim and prologue (until the first slice is in LDS), K loop and epilogue
-    (from the last slice to the stores issued)."""
+    claim and prologue (until the first slice is in LDS), K loop (its first 8
+    slices, the middle, the last 8) and epilogue (from the last slice to the
+    stores issued)."""
     import ctypes
 
     import numpy as np
@@ -622,7 +623,7 @@ def bench_tile_timeline(args, wl) -> int:
         raise RuntimeError("muon_tile_trace_clear failed")
     nsa.ns_batched(xs, steps=wl.steps, coeffs=wl.coeffs, out=outs, workspace=ws)
     torch.cuda.synchronize(dev)
-    nslot, nblk, nword = len(TRACE_SLOTS), 65536, 5
+    nslot, nblk, nword = len(TRACE_SLOTS), 65536, 7
     buf = np.zeros(nslot * nblk * nword, dtype=np.uint64)
     lib.muon_tile_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     if lib.muon_tile_trace_read(buf.ctypes.data, buf.nbytes) != 0:
@@ -658,12 +659,20 @@ def bench_tile_timeline(args, wl) -> int:
         dur = (end[work] - start[work]) / 100.0
         # off-diagonal tiles: start -> K loop -> epilogue (claim and prologue, K loop, epilogue)
         kb, ke = rec[:, 3].astype(np.int64), rec[:, 4].astype(np.int64)
+        k8, kl = rec[:, 5].astype(np.int64), rec[:, 6].astype(np.int64)
         ph = work & (kb > 0) & (ke >= kb)
         phases = None
         if np.any(ph):
             phases = {k: [round(float(np.percentile(v, q)), 2) for q in (10, 50, 90)] for k, v in (
                 ("prologue", (kb[ph] - start[ph]) / 100.0), ("k_loop", (ke[ph] - kb[ph]) / 100.0),
                 ("epilogue", (end[ph] - ke[ph]) / 100.0))}
+            # tiles with at least 16 slices: first 8, middle, last 8 slices of the K loop
+            sp = ph & (k8 >= kb) & (kl >= k8) & (ke >= kl)
+            if np.any(sp):
+                for k, v in (("k_first8", (k8[sp] - kb[sp]) / 100.0),
+                             ("k_middle", (kl[sp] - k8[sp]) / 100.0),
+                             ("k_last8", (ke[sp] - kl[sp]) / 100.0)):
+                    phases[k] = [round(float(np.percentile(v, q)), 2) for q in (10, 50, 90)]
         result["launches"][name] = {
             "workgroups": int(len(rec)), "tiles": int(work.sum()), "cus": int(len(busy)),
             "truncated": bool(len(rec) >= nblk),  # a larger grid than the timeline holds
@@ -723,7 +732,7 @@ def main(argv=None) -> int:
                          "timeline build")
     ap.add_argument("--timeline-raw", default="",
                     help="with --tile-timeline: also save the raw per-workgroup records (numpy, "
-                         "slots x workgroups x [start, end, ids, K loop start, K loop end])")
+                         "slots x workgroups x [start, end, ids, K loop start and end, slices 8 and nk-8])")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known "
                          "byte count for scaling hardware traffic counters)")

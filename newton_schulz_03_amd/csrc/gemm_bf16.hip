@@ -35,10 +35,12 @@ namespace muon {
 // hardware ids of the CU it ran on (HW_ID: CU and shader engine; XCC_ID: the
 // XCD), and, for off-diagonal tiles, the moments its K loop began (first
 // slice in LDS, after the barrier) and ended (last MFMA issued and every load
-// landed, after the barrier): prologue, K loop and epilogue of each tile.
+// landed, after the barrier): prologue, K loop and epilogue of each tile; and
+// the starts of its slices 8 and nk - 8, which split the K loop into its
+// first 8 slices, the middle and the last 8.
 [[maybe_unused]] constexpr int kTraceSlots = 4;
 [[maybe_unused]] constexpr int kTraceBlocks = 65536;
-[[maybe_unused]] constexpr int kTraceWords = 5;  // start, end, ids, K loop start, K loop end
+[[maybe_unused]] constexpr int kTraceWords = 7;  // start, end, ids, K loop start and end, slices 8 and nk-8
 #ifdef MUON_TILE_TRACE
 __device__ unsigned long long g_tile_trace[kTraceSlots * kTraceBlocks * kTraceWords];
 #endif
@@ -52,7 +54,8 @@ __device__ __forceinline__ void trace_start(int slot) {
 #endif
 }
 
-// word 3: the K loop begins, word 4: it has ended (single-tile kernels only)
+// word 3: the K loop begins, 4: it has ended, 5 and 6: slices 8 and nk - 8
+// begin (single-tile kernels only)
 __device__ __forceinline__ void trace_phase(int slot, int word) {
 #ifdef MUON_TILE_TRACE
   if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks)
@@ -577,6 +580,10 @@ __device__ __forceinline__ void gemm_tile(const LaunchCtx& c, const GemmArgs& g,
   // would be, and the wide kernel, which adds its terms in the same order,
   // would spill).
   auto slice = [&](int kt, auto R) {
+    if constexpr (!LOOP) {
+      if (kt == 8) trace_phase(MODE == GM_PROD ? 3 : MODE, 5);
+      if (kt == nk - 8) trace_phase(MODE == GM_PROD ? 3 : MODE, 6);
+    }
     const int st = kt & (NST - 1);
     const char* stage = smem + st * STAGEB;
     const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
@@ -880,6 +887,8 @@ __device__ __forceinline__ void gemm_tile_wide(const LaunchCtx& c, const GemmArg
   // and every spill reload then waited for vmcnt(0), since the compiler cannot
   // count the loads in the inline assembly, draining the operand prefetch.
   auto slice = [&](int kt, auto R) {
+    if (kt == 8) trace_phase(2, 5);
+    if (kt == nk - 8) trace_phase(2, 6);
     const char* stage = smem + (kt & (NST - 1)) * STAGEW;
     const int ks = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
     const uint32_t fill = ring + ((kt + NST - 1) & (NST - 1)) * STAGEW;
