@@ -89,6 +89,11 @@ __device__ __forceinline__ void add_term(f32x16_t (&acc)[4][4], const TileRef& t
   const int64_t ld = MODE == GM_PROD ? tr.d.l_pad : tr.d.s_pad;
   const int64_t r0 = MODE == GM_PROD ? lp.row0 : lp.rq0;
   const int64_t c0 = MODE == GM_PROD ? lp.col0 : lp.cp0;
+  // the tile's origin (uniform) and this lane's offsets within the tile
+  const int64_t tr0 = static_cast<int64_t>(MODE == GM_PROD ? tr.ti : tr.tj) * kTile;
+  const int64_t tc0 = static_cast<int64_t>(MODE == GM_PROD ? tr.tj : tr.ti) * kTile;
+  const uint16_t* const org = src + slab_off(tr0, tc0, ld);
+  const int q0 = static_cast<int>(r0 - tr0), p0 = static_cast<int>(c0 - tc0);
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     float x[4][4][4];
@@ -96,7 +101,7 @@ __device__ __forceinline__ void add_term(f32x16_t (&acc)[4][4], const TileRef& t
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg)
-        load4<uint16_t>(src + slab_off(r0 + ni * 32, c0 + mi * 32 + 8 * gg, ld), x[ni][gg]);
+        load4<uint16_t>(org + slab_local(q0 + ni * 32, p0 + mi * 32 + 8 * gg), x[ni][gg]);
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
