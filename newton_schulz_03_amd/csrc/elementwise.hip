@@ -192,9 +192,10 @@ __global__ __launch_bounds__(kThreads) void k_prepare(LaunchCtx c, ElemParams p)
   __shared__ int slot;
   const int32_t* pre = c.prefix + PH_PREPARE * (c.batch + 1);
   const int32_t b = blockIdx.x;
-  const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, &slot));
+  const int32_t per = c.per[PH_PREPARE];  // a uniform batch: the matrix by one division
+  const int j = per > 0 ? b / per : __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, &slot));
   const MatDesc& d = c.desc[j];
-  const int32_t t = b - pre[j];
+  const int32_t t = per > 0 ? b - j * per : b - pre[j];
   T* xu = static_cast<T*>(iterate(d, 0));  // the first iterate buffer, holding U
   float acc;
   if (!d.tall) {

@@ -683,11 +683,13 @@ __device__ __forceinline__ void mfma_guard(f32x16_t (&v)[2][4]) {
 // Tile number b of a wide product launch -> (matrix, tile), as decode_tile.
 __device__ __forceinline__ TileRef decode_wide(const LaunchCtx& c, int32_t b, int* slot) {
   const int32_t* pre = c.prefix + PH_PRODW * (c.batch + 1);
-  const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
+  const int32_t per = c.per[PH_PRODW];  // as in decode_tile
+  const int j = per > 0 ? b / per : __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;
   r.d = load_const(c.desc + j);
   r.mat = j;
-  prod_tile(b - load_const(pre + j), r.d.s_pad / kTile, r.d.l_pad / kTileW, r.ti, r.tj);
+  prod_tile(per > 0 ? b - j * per : b - load_const(pre + j), r.d.s_pad / kTile,
+            r.d.l_pad / kTileW, r.ti, r.tj);
   return r;
 }
 

@@ -257,12 +257,16 @@ __device__ __forceinline__ int32_t claim_tile(const XcdSplit& s, const LaunchCtx
 // cooperatively, through `slot` in LDS.
 template <int MODE>
 __device__ __forceinline__ TileRef decode_tile(const LaunchCtx& c, int32_t b, int* slot) {
-  const int32_t* pre = c.prefix + (MODE == GM_PROD ? PH_PROD : PH_SYM) * (c.batch + 1);
-  const int j = __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
+  constexpr int ph = MODE == GM_PROD ? PH_PROD : PH_SYM;
+  const int32_t* pre = c.prefix + ph * (c.batch + 1);
+  // a uniform batch: the matrix by one division, without the prefix table's
+  // loads and the lookup's barrier on the tile's way to its first loads
+  const int32_t per = c.per[ph];
+  const int j = per > 0 ? b / per : __builtin_amdgcn_readfirstlane(locate_matrix(pre, c.batch, b, slot));
   TileRef r;
   r.d = load_const(c.desc + j);
   r.mat = j;
-  const int32_t t = b - load_const(pre + j);
+  const int32_t t = per > 0 ? b - j * per : b - load_const(pre + j);
   const int32_t ts = r.d.s_pad / kTile;
   if constexpr (MODE == GM_PROD) {
     prod_tile(t, ts, r.d.l_pad / kTile, r.ti, r.tj);

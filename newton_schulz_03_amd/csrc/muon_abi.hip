@@ -43,6 +43,7 @@ struct Plan {
   std::vector<size_t> mat_off;      // byte offset of matrix i's buffers
   std::vector<int32_t> prefix;      // NPHASE x (batch + 1)
   int32_t totals[NPHASE] = {};
+  int32_t per[NPHASE] = {};         // blocks per matrix where every matrix has as many; else 0
   XcdSplit split_gram{}, split_poly{}, split_prod{};  // matrix-core launches over the XCDs
   // Wide product tiles (256 x kTileW): every matrix's padded long side is a
   // multiple of kTileW.  Then the products that store the iterate use them.
@@ -195,8 +196,14 @@ int32_t make_plan(int32_t batch, const int64_t* rows, const int64_t* cols, int32
     }
   }
   for (int ph = 0; ph < NPHASE; ++ph) {
+    const int32_t* pre = pl.prefix.data() + static_cast<size_t>(ph) * (batch + 1);
     pl.prefix[static_cast<size_t>(ph) * (batch + 1) + batch] = static_cast<int32_t>(tot[ph]);
     pl.totals[ph] = static_cast<int32_t>(tot[ph]);
+    // a uniform batch: the kernels find a block's matrix by one division
+    const int32_t first = batch > 0 ? pre[1] - pre[0] : 0;
+    bool same = first > 0;
+    for (int32_t i = 1; same && i < batch; ++i) same = pre[i + 1] - pre[i] == first;
+    pl.per[ph] = same ? first : 0;
   }
   int32_t st;
   pl.order.clear();
@@ -527,6 +534,7 @@ int32_t run(const Plan& pl, char* ws, hipStream_t stream, const ElemParams& ep,
   };
   c.batch = pl.batch;
   c.max_blocks = ns.cu_budget;
+  for (int ph = 0; ph < NPHASE; ++ph) c.per[ph] = pl.per[ph];
   c.stream = stream;
   hipError_t e;
   {

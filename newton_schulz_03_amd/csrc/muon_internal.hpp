@@ -110,6 +110,9 @@ struct LaunchCtx {
   int32_t* sched_next;     // device: the next one's, which this launch zeroes
   int32_t batch;
   int32_t max_blocks;      // matrix-core launches: most workgroups resident (0: one per tile)
+  // per phase: the blocks of every matrix when all matrices have the same
+  // number (then block b belongs to matrix b / per[ph]); 0 for a ragged batch
+  int32_t per[NPHASE];
   hipStream_t stream;
 };
 

@@ -222,6 +222,17 @@ int main() {
       k_long[i] = pl.desc[i].l_pad / 32;
       k_short[i] = pl.desc[i].s_pad / 32;
     }
+    // per[ph]: set exactly when every matrix has as many blocks, and then
+    // block b lies in matrix b / per[ph] of the prefix table
+    for (int ph = 0; ph < NPHASE; ++ph) {
+      const int32_t* pre = pl.prefix.data() + static_cast<size_t>(ph) * (batch + 1);
+      bool same = pre[1] - pre[0] > 0;
+      for (int i = 1; i < batch; ++i) same = same && pre[i + 1] - pre[i] == pre[1] - pre[0];
+      expect(pl.per[ph] == (same ? pre[1] - pre[0] : 0), "per-matrix block count wrong", trial);
+      if (pl.per[ph] > 0)
+        for (int i = 0; i <= batch; ++i)
+          expect(pre[i] == i * pl.per[ph], "uniform prefix not a multiple", trial);
+    }
     check_split(pl.split_gram, sym, k_long, pl.order, false, trial);
     check_split(pl.split_poly, sym, k_short, pl.order, true, trial);
     check_split(pl.split_prod, prod, k_short, pl.order, true, trial);
@@ -279,6 +290,15 @@ int main() {
     expect(pl.wide_prod && pl.split_prodw.grid == 8 * (1536 + 96), "uniform wide grid", -1);
     for (int x = 0; x <= kXcd; ++x)
       expect(pl.split_prodw.lo[x] == 1536 * x, "uniform wide ranges", -1);
+    // 8 x 24 product tiles, 36 upper tiles, 8 x 16 wide tiles per matrix
+    expect(pl.per[PH_PROD] == 192 && pl.per[PH_SYM] == 36 && pl.per[PH_PRODW] == 128,
+           "uniform per-matrix block counts", -1);
+    // one matrix of another shape makes every count ragged
+    r[40] = 1024;
+    Plan pr;
+    expect(make_plan(96, r.data(), c.data(), MUON_BF16, pr) == MUON_OK, "ragged plan", -1);
+    expect(pr.per[PH_PROD] == 0 && pr.per[PH_SYM] == 0 && pr.per[PH_PRODW] == 0,
+           "ragged per-matrix block counts", -1);
   }
   // the chunks of a step with the momentum in host memory: at most kMaxChunks
   // contiguous chunks covering every matrix once, each chunk's momentum inside
