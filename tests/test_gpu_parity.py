@@ -90,6 +90,20 @@ def test_ns_one_large_among_many_small(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("shapes", [
+    [(1100, 2304)] * 6,                      # every phase uniform: tiles find their matrix by division
+    [(2304, 1100)] * 3 + [(1100, 2304)] * 3,  # the matrix-core phases uniform, the prepare blocks not
+    [(1100, 2304)] * 5 + [(1100, 1800)],      # one long side off: every phase ragged again
+])
+def test_ns_uniform_and_mixed_phases(dtype, shapes):
+    """A batch of equal matrices takes a per-matrix block count instead of the
+    prefix-table lookup; tall and wide matrices of the same sides share the
+    matrix-core phases' counts but not the momentum pass's.  Multi-tile
+    matrices with ragged edges, checked per block against the oracle."""
+    _ns_check(dtype, shapes)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("eps", [0.0, 1.0])
 @pytest.mark.parametrize("steps", [0, 5])
 def test_eps_enters_the_normalization(dtype, eps, steps):
