@@ -70,6 +70,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build the HIP library first "
             "(python -m newton_schulz_03_amd.build, or __graft_entry__.build())")
+    # torch brings its own copy of the HIP runtime.  Loaded first, it serves
+    # this library too (one runtime per process); loaded after this library,
+    # the library's runtime reported no device (hipErrorNoDevice) on MI355X.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     i32, i64p, vpp, vp, sz = (ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_size_t)
